@@ -1,0 +1,321 @@
+"""Decode-step benchmark: Dual-QK INT2 pruned decode attention at 128K context.
+
+One step = the whole hot path for one new token of every sequence in the batch:
+append (key transform + 2-bit quantize/pack of the new K/V), query transform +
+channel selection, pruned decode attention with split-K and combine.
+Workload: batch 1, 32 query / 8 KV heads, head_dim 128, 131072-token context,
+bf16 inputs, 40% query-channel sparsity (seeded synthetic data).
+
+Several copies of the cache are kept in HBM and the steps rotate through them,
+so consecutive steps never find their cache in the 256 MB Infinity Cache: the
+measured rate is HBM streaming.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------- byte accounting
+
+def decode_bytes(idx: np.ndarray, lengths, hkv: int, d: int, keep: int) -> int:
+    """Algorithmic bytes of one pruned decode: per (row, KV head) with union U of kept
+    channels >= 1 over the group's heads, T tokens, Tb = 32*floor(T/32):
+    |U|*Tb/4 (codes) + 2|U|*Tb/32 (scales) + 2T (channel 0) + 4|U|(T-Tb) (tail)
+    + d*ceil(T/4) (value codes) + 2T*d/32 (value scales), plus per query head
+    q' and indices of kept channels (8*keep) and the fp32 output (4d)."""
+    batch, hq, _ = idx.shape
+    grp = hq // hkv
+    total = 0
+    for b in range(batch):
+        t = int(lengths[b])
+        tb = t // 32 * 32
+        for g in range(hkv):
+            sel = idx[b, g * grp:(g + 1) * grp].ravel()
+            u = len(set(int(c) for c in sel if c != 0))
+            total += u * tb // 4 + 2 * u * tb // 32 + 2 * t + 4 * u * (t - tb)
+            total += d * ((t + 3) // 4) + 2 * t * d // 32
+            total += grp * ((8 * keep if t > 0 else 0) + 4 * d)
+    return total
+
+
+def select_bytes(batch: int, hq: int, hkv: int, d: int, keep: int, in_bytes: int) -> int:
+    """q in, A of every KV head, q' and indices out."""
+    return batch * hq * d * in_bytes + hkv * d * d * 4 + batch * hq * (4 * d + 4 * keep)
+
+
+def append_bytes(batch: int, hkv: int, d: int, positions, in_bytes: int) -> int:
+    """One new token per (row, KV head): k and v in, B_g in, channel 0, tail row,
+    the d value words read and written, value scales; a token closing its
+    32-token group also reads 31 tail rows and writes (d-1) 8-byte code runs and
+    (d-1) key scales."""
+    total = 0
+    for b in range(batch):
+        p = int(positions[b])
+        per = 2 * d * in_bytes + d * d * 4 + 2 + 4 * d + 8 * d + 2 * (d // 32)
+        if p % 32 == 31:
+            per += 31 * 4 * d + (d - 1) * 10
+        total += hkv * per
+    return total
+
+
+# ----------------------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(wl, a, b, keep, sm, budget_s: float = 20.0):
+    """The oracle, as written, on a bounded sample: one KV head (its G query heads)
+    of the workload at full context: untimed cache build, then timed repeats of
+    append-1 + select + decode with OpenMP over query heads.  Rate in GB/s of the
+    same algorithmic bytes."""
+    import oracle
+    ncpu = os.cpu_count() or 1
+    threads = max(1, min(ncpu, 16))
+    os.environ.setdefault("OMP_NUM_THREADS", str(threads))
+    g = 0
+    t_ctx = int(wl.ctx[0])
+    sub = W.custom("cpu-sample", wl.cid, 1, wl.group, 1, wl.d, [t_ctx], wl.cap, wl.dtype)
+    kk, vv = W.unit_kv(wl, 0, g, 0, t_ctx)
+    c = oracle.Cache(1, 1, wl.d, wl.cap)
+    t0 = time.time()
+    c.append(kk[None, None], vv[None, None], b[g:g + 1], [t_ctx])
+    build_s = time.time() - t0
+    q = W.queries(wl, 0)[:, g * wl.group:(g + 1) * wl.group]
+    knew = np.random.default_rng(7).standard_normal((1, 1, 1, wl.d)).astype(np.float32)
+    reps, spent, nbytes = 0, 0.0, 0
+    while spent < budget_s and reps < 50:
+        t0 = time.perf_counter()
+        c.append(knew, knew, b[g:g + 1], [1])
+        qp, idx = oracle.queries(q, a[g:g + 1], 1, keep)
+        c.decode(qp, idx, sm, nthreads=threads)
+        spent += time.perf_counter() - t0
+        nbytes += (decode_bytes(idx, c.lengths, 1, wl.d, keep)
+                   + select_bytes(1, wl.group, 1, wl.d, keep, 2)
+                   + append_bytes(1, 1, wl.d, c.lengths - 1, 2))
+        reps += 1
+    del sub
+    return {"value": round(nbytes / spent / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"1 of {wl.hkv} KV heads ({wl.group} query heads) of the workload at "
+                       f"{t_ctx} tokens: append 1 + select + decode, {reps} repeats in "
+                       f"{spent:.1f}s (cache build {build_s:.1f}s untimed); OpenMP over query heads"),
+            "ms_per_unit_step": round(1e3 * spent / reps, 2)}
+
+
+# ----------------------------------------------------------------------------- GPU
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--sparsity", type=int, default=40)
+    ap.add_argument("--copies", type=int, default=6, help="cache copies rotated through")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--split", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import bit_quantized_decode_dqk_amd as M
+
+    torch.cuda.set_device(0)
+    dev = "cuda"
+    wl = W.workload("ctx128k", steps=256)
+    keep = M.keep_for_sparsity(wl.d, args.sparsity)
+    sm = W.default_sm_scale(wl.d)
+    ctx = int(wl.ctx[0])
+    log(f"workload {wl.describe()}, keep {keep}")
+
+    t0 = time.time()
+    a, b = W.transforms(wl)
+    kscale = W.key_scales(wl)
+    k_pre = np.zeros((wl.batch, wl.hkv, ctx, wl.d), dtype=np.uint16)
+    v_pre = np.zeros_like(k_pre)
+    for bb in range(wl.batch):
+        for g in range(wl.hkv):
+            kk, vv = W.unit_kv(wl, bb, g, 0, ctx, kscale)
+            k_pre[bb, g] = W.bf16_bits(kk)
+            v_pre[bb, g] = W.bf16_bits(vv)
+    log(f"inputs generated in {time.time() - t0:.1f}s")
+
+    def to_bf16(bits):
+        return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    a_d = torch.from_numpy(a).to(dev)
+    b_d = torch.from_numpy(b).to(dev)
+    k_d, v_d = to_bf16(k_pre), to_bf16(v_pre)
+    caches = [M.Cache(wl.batch, wl.hkv, wl.d, wl.cap) for _ in range(args.copies)]
+    M.transform_quantize_append(caches[0], k_d, v_d, b_d,
+                                torch.full((wl.batch,), ctx, dtype=torch.int32, device=dev))
+    for c in caches[1:]:
+        for name, t in caches[0].planes().items():
+            getattr(c, name).copy_(t)
+    torch.cuda.synchronize()
+    log(f"{args.copies} cache copies of {caches[0].nbytes() / 1e6:.1f} MB built")
+
+    nstep = args.warmup + args.steps
+    step_kv = torch.randn((nstep, wl.batch, wl.hkv, 1, wl.d), device=dev).to(torch.bfloat16)
+    step_q = torch.stack([to_bf16(W.bf16_bits(W.queries(wl, i))) for i in range(nstep)])
+    ones = torch.ones((wl.batch,), dtype=torch.int32, device=dev)
+    qp = torch.empty((wl.batch, wl.hq, wl.d), dtype=torch.float32, device=dev)
+    idx = torch.empty((wl.batch, wl.hq, keep), dtype=torch.int32, device=dev)
+    out = torch.empty((wl.batch, wl.hq, wl.d), dtype=torch.float32, device=dev)
+    ws = torch.empty(M.decode_workspace_bytes(caches[0], wl.hq, args.split), dtype=torch.uint8,
+                     device=dev)
+
+    # algorithmic bytes of every step (selections are deterministic given q)
+    lens = [np.full(wl.batch, ctx, dtype=np.int64) for _ in caches]
+    step_bytes, dec_bytes = [], []
+    for i in range(nstep):
+        ci = i % len(caches)
+        M.select_channels(step_q[i], a_d, wl.hkv, keep, qp, idx)
+        idx_np = idx.cpu().numpy()
+        pos = lens[ci].copy()
+        lens[ci] += 1
+        db = decode_bytes(idx_np, lens[ci], wl.hkv, wl.d, keep)
+        dec_bytes.append(db)
+        step_bytes.append(db + select_bytes(wl.batch, wl.hq, wl.hkv, wl.d, keep, 2)
+                          + append_bytes(wl.batch, wl.hkv, wl.d, pos, 2))
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nstep)]
+
+    def step(i):
+        c = caches[i % len(caches)]
+        e = ev[i]
+        e[0].record()
+        M.transform_quantize_append(c, step_kv[i], step_kv[i], b_d, ones)
+        M.select_channels(step_q[i], a_d, wl.hkv, keep, qp, idx)
+        e[1].record()
+        M.decode_attention(c, qp, idx, sm, args.split, out, ws)
+        e[2].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.warmup, nstep):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_step = 1e3 * wall / args.steps
+    timed = range(args.warmup, nstep)
+    dec_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in timed]
+    pre_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in timed]
+    tot_bytes = sum(step_bytes[i] for i in timed)
+    gbs = tot_bytes / wall / 1e9
+    dec_avg_ms = float(np.mean(dec_ms))
+    dec_gbs = float(np.mean([dec_bytes[i] for i in timed])) / (dec_avg_ms * 1e-3) / 1e9
+    log(f"step {ms_step * 1e3:.1f} us, decode (partial+combine) {dec_avg_ms * 1e3:.1f} us "
+        f"(p10 {np.percentile(dec_ms, 10) * 1e3:.1f} p90 {np.percentile(dec_ms, 90) * 1e3:.1f}), "
+        f"append+select {np.mean(pre_ms) * 1e3:.1f} us, {gbs:.0f} GB/s step, {dec_gbs:.0f} GB/s decode")
+
+    extras = {}
+    if not args.no_extras:
+        extras = run_extras(M, torch, wl, caches, a_d, step_q, qp, idx, out, ws, k_d, v_d, sm,
+                            args, dec_avg_ms)
+
+    result = {
+        "metric": "decode attention effective HBM GB/s + tokens/s at 128K ctx, INT2, 40% sparsity",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; bf16 q/k/v, log-uniform key channel scales, channel 0 x8)",
+        "config": {"workload": "ctx128k: batch 1, 32/8 heads, head_dim 128, context 131072, "
+                               f"INT2 K/V groups of 32, {args.sparsity}% query-channel sparsity, "
+                               "step = append 1 token + select + decode",
+                   "global_batch": wl.batch, "seq_len": ctx, "parallelism": "none (1 GPU)",
+                   "keep": keep, "cache_copies": args.copies},
+        "tokens_per_s": round(wl.batch / (ms_step * 1e-3), 1),
+        "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "pruned decode (partial + combine launches)",
+                     "bytes_per_launch": int(np.mean([dec_bytes[i] for i in timed])),
+                     "avg_us": round(dec_avg_ms * 1e3, 2)},
+    }
+    if extras:
+        result["extras"] = extras
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        result["cpu_baseline"] = cpu_baseline(wl, a, b, keep, sm)
+    print(json.dumps(result), flush=True)
+
+
+def run_extras(M, torch, wl, caches, a_d, step_q, qp, idx, out, ws, k_d, v_d, sm, args,
+               dec_avg_ms):
+    """Decode-only timings for the sparsity sweep and the unpruned BF16 comparator."""
+    res = {}
+    for s in (0, 40, 60):
+        keep = M.keep_for_sparsity(wl.d, s)
+        qp2 = torch.empty_like(qp)
+        idx2 = torch.empty((wl.batch, wl.hq, keep), dtype=torch.int32, device=qp.device)
+        M.select_channels(step_q[0], a_d, wl.hkv, keep, qp2, idx2)
+        idx_np = idx2.cpu().numpy()
+        lens = caches[0].lengths.cpu().numpy()
+        nb = decode_bytes(idx_np, lens, wl.hkv, wl.d, keep)
+        ts = []
+        for i in range(30):
+            c = caches[i % len(caches)]
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            M.decode_attention(c, qp2, idx2, sm, args.split, out, ws)
+            e1.record()
+            ts.append((e0, e1))
+        torch.cuda.synchronize()
+        us = float(np.mean([a.elapsed_time(b) for a, b in ts[5:]])) * 1e3
+        res[f"decode_s{s}"] = {"us": round(us, 2), "GB/s": round(nb / us / 1e3, 1), "bytes": nb}
+    # unpruned bf16 decode over the raw cache (2 copies rotate: 537 MB each)
+    ctx = int(wl.ctx[0])
+    k2, v2 = k_d.clone(), v_d.clone()
+    pairs = [(k_d, v_d), (k2, v2)]
+    lengths = torch.full((wl.batch,), ctx, dtype=torch.int32, device=qp.device)
+    wsb = torch.empty(M.bf16_decode_workspace_bytes(wl.batch, wl.hq, wl.hkv, wl.d, ctx),
+                      dtype=torch.uint8, device=qp.device)
+    ts = []
+    for i in range(30):
+        kk, vv = pairs[i % 2]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        M.bf16_decode_attention(step_q[i % len(step_q)], kk, vv, lengths, sm, 0, out, wsb)
+        e1.record()
+        ts.append((e0, e1))
+    torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(b) for a, b in ts[5:]])) * 1e3
+    nb = wl.batch * wl.hkv * ctx * wl.d * 2 * 2 + wl.batch * wl.hq * wl.d * (2 + 4)
+    res["bf16_unpruned_decode"] = {"us": round(us, 2), "GB/s": round(nb / us / 1e3, 1),
+                                   "bytes": nb,
+                                   "speedup_int2_pruned_vs_bf16": round(us / (dec_avg_ms * 1e3), 3)}
+    del k2, v2
+    return res
+
+
+if __name__ == "__main__":
+    main()

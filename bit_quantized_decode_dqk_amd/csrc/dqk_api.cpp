@@ -1,0 +1,182 @@
+// Host side of the C ABI: validation of everything the host can see, workspace
+// sizing, and dispatch to the kernels.  Nothing here allocates, synchronizes or
+// keeps state; an invalid call returns before any HIP call is made, so every
+// error path can be exercised on a machine without a GPU.
+#include <math.h>
+#include <stdint.h>
+
+#include "dqk_internal.h"
+
+namespace {
+
+using dqk::kDefaultSplit;
+using dqk::kGroup;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool supported_dim(int d) { return d == 64 || d == 128; }
+
+bool supported_group(int hq, int hkv) {
+  if (hkv <= 0 || hq <= 0 || hq % hkv != 0) return false;
+  const int g = hq / hkv;
+  return g == 1 || g == 2 || g == 4 || g == 8;
+}
+
+// Shape and pointers of a cache; returns DQK_OK or the first problem found.
+dqk_status check_cache(const dqk_cache *c) {
+  if (!c) return DQK_ERR_INVALID;
+  if (c->batch <= 0 || c->num_kv_heads <= 0 || c->capacity <= 0) return DQK_ERR_INVALID;
+  if (c->capacity % kGroup != 0) return DQK_ERR_INVALID;
+  if (!supported_dim(c->head_dim)) return DQK_ERR_UNSUPPORTED;
+  const void *planes[] = {c->k_codes, c->k_scales, c->k_ch0, c->k_tail,
+                          c->v_codes, c->v_scales, c->lengths};
+  for (const void *p : planes)
+    if (!p || !aligned16(p)) return DQK_ERR_INVALID;
+  // element counts must stay addressable by 32-bit grid arithmetic per unit
+  if ((int64_t)c->batch * c->num_kv_heads > (1 << 24)) return DQK_ERR_INVALID;
+  return DQK_OK;
+}
+
+dqk_status from_hip(hipError_t e) { return e == hipSuccess ? DQK_OK : DQK_ERR_HIP; }
+
+int pick_split(int split) { return split == 0 ? kDefaultSplit : split; }
+
+bool valid_split(int split) { return split == 0 || (split >= kGroup && split % kGroup == 0); }
+
+size_t decode_ws_bytes(int batch, int hkv, int hq, int d, int tokens, int split) {
+  const int nsplit = dqk::num_splits(tokens, pick_split(split));
+  return (size_t)batch * hkv * nsplit * (size_t)(hq / hkv) * dqk::partial_floats(d) * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *dqk_status_str(dqk_status s) {
+  switch (s) {
+    case DQK_OK: return "ok";
+    case DQK_ERR_INVALID: return "invalid argument";
+    case DQK_ERR_UNSUPPORTED: return "unsupported shape";
+    case DQK_ERR_WORKSPACE: return "workspace missing or too small";
+    case DQK_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+dqk_status dqk_cache_plane_bytes(int32_t batch, int32_t hkv, int32_t d, int32_t cap,
+                                 size_t *out) {
+  if (!out || batch <= 0 || hkv <= 0 || cap <= 0 || cap % kGroup != 0) return DQK_ERR_INVALID;
+  if (!supported_dim(d)) return DQK_ERR_UNSUPPORTED;
+  const size_t u = (size_t)batch * hkv;
+  out[0] = u * d * (cap / 4);                   // k_codes
+  out[1] = u * d * (cap / kGroup) * 2;          // k_scales
+  out[2] = u * cap * 2;                         // k_ch0
+  out[3] = u * kGroup * d * 4;                  // k_tail
+  out[4] = u * (cap / 16) * d * 4;              // v_codes
+  out[5] = u * cap * (d / kGroup) * 2;          // v_scales
+  out[6] = (size_t)batch * 4;                   // lengths
+  return DQK_OK;
+}
+
+dqk_status dqk_transform_quantize_append(const dqk_cache *cache, const void *k_new,
+                                         const void *v_new, dqk_dtype dtype, const float *bmat,
+                                         const int32_t *n_new, int32_t max_new,
+                                         dqk_stream_t stream) {
+  dqk_status st = check_cache(cache);
+  if (st != DQK_OK) return st;
+  if (dtype != DQK_F32 && dtype != DQK_BF16) return DQK_ERR_INVALID;
+  if (!k_new || !v_new || !bmat || !n_new || max_new < 0) return DQK_ERR_INVALID;
+  if (max_new == 0) return DQK_OK;
+  if ((int64_t)max_new > cache->capacity) return DQK_ERR_INVALID;
+  return from_hip(dqk::launch_append(*cache, k_new, v_new, dtype == DQK_BF16, bmat, n_new, max_new,
+                                     reinterpret_cast<hipStream_t>(stream)));
+}
+
+dqk_status dqk_select_channels(const void *q, dqk_dtype dtype, const float *amat, int32_t batch,
+                               int32_t hq, int32_t hkv, int32_t d, int32_t keep, float *q_prime,
+                               int32_t *sel_idx, dqk_stream_t stream) {
+  if (!q || !amat || !q_prime || !sel_idx) return DQK_ERR_INVALID;
+  if (dtype != DQK_F32 && dtype != DQK_BF16) return DQK_ERR_INVALID;
+  if (batch <= 0 || hq <= 0 || hkv <= 0 || hq % hkv != 0) return DQK_ERR_INVALID;
+  if (!supported_dim(d)) return DQK_ERR_UNSUPPORTED;
+  if (keep < 1 || keep > d) return DQK_ERR_INVALID;
+  if ((int64_t)batch * hq > (1 << 30)) return DQK_ERR_INVALID;
+  return from_hip(dqk::launch_select(q, dtype == DQK_BF16, amat, batch, hq, hkv, d, keep, q_prime,
+                                     sel_idx, reinterpret_cast<hipStream_t>(stream)));
+}
+
+dqk_status dqk_decode_workspace_bytes(const dqk_cache *cache, int32_t hq, int32_t split,
+                                      size_t *out) {
+  if (!out) return DQK_ERR_INVALID;
+  dqk_status st = check_cache(cache);
+  if (st != DQK_OK) return st;
+  if (!supported_group(hq, cache->num_kv_heads)) return DQK_ERR_UNSUPPORTED;
+  if (!valid_split(split)) return DQK_ERR_INVALID;
+  *out = decode_ws_bytes(cache->batch, cache->num_kv_heads, hq, cache->head_dim, cache->capacity,
+                         split);
+  return DQK_OK;
+}
+
+dqk_status dqk_decode_attention(const dqk_cache *cache, const float *q_prime,
+                                const int32_t *sel_idx, int32_t hq, int32_t keep, float sm_scale,
+                                int32_t split, float *out, void *workspace, size_t ws_bytes,
+                                dqk_stream_t stream) {
+  dqk_status st = check_cache(cache);
+  if (st != DQK_OK) return st;
+  if (!q_prime || !sel_idx || !out) return DQK_ERR_INVALID;
+  if (!supported_group(hq, cache->num_kv_heads)) {
+    if (hq <= 0 || hq % cache->num_kv_heads != 0) return DQK_ERR_INVALID;
+    return DQK_ERR_UNSUPPORTED;
+  }
+  if (keep < 1 || keep > cache->head_dim) return DQK_ERR_INVALID;
+  if (!isfinite(sm_scale)) return DQK_ERR_INVALID;
+  if (!valid_split(split)) return DQK_ERR_INVALID;
+  const size_t need = decode_ws_bytes(cache->batch, cache->num_kv_heads, hq, cache->head_dim,
+                                      cache->capacity, split);
+  if (!workspace || ws_bytes < need || !aligned16(workspace)) return DQK_ERR_WORKSPACE;
+  return from_hip(dqk::launch_decode(*cache, q_prime, sel_idx, hq, keep, sm_scale,
+                                     pick_split(split), out, static_cast<float *>(workspace),
+                                     reinterpret_cast<hipStream_t>(stream)));
+}
+
+dqk_status dqk_dequant_reference(const dqk_cache *cache, float *k_out, float *v_out,
+                                 dqk_stream_t stream) {
+  dqk_status st = check_cache(cache);
+  if (st != DQK_OK) return st;
+  if (!k_out || !v_out) return DQK_ERR_INVALID;
+  return from_hip(dqk::launch_dequant(*cache, k_out, v_out, reinterpret_cast<hipStream_t>(stream)));
+}
+
+dqk_status dqk_bf16_decode_workspace_bytes(int32_t batch, int32_t hq, int32_t hkv, int32_t d,
+                                           int32_t ld_t, int32_t split, size_t *out) {
+  if (!out || batch <= 0 || ld_t <= 0) return DQK_ERR_INVALID;
+  if (!supported_dim(d)) return DQK_ERR_UNSUPPORTED;
+  if (!supported_group(hq, hkv)) return DQK_ERR_UNSUPPORTED;
+  if (!valid_split(split)) return DQK_ERR_INVALID;
+  *out = decode_ws_bytes(batch, hkv, hq, d, ld_t, split);
+  return DQK_OK;
+}
+
+dqk_status dqk_bf16_decode_attention(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                     const int32_t *lengths, int32_t batch, int32_t hq,
+                                     int32_t hkv, int32_t d, int32_t ld_t, float sm_scale,
+                                     int32_t split, float *out, void *workspace, size_t ws_bytes,
+                                     dqk_stream_t stream) {
+  if (!q || !k || !v || !lengths || !out) return DQK_ERR_INVALID;
+  if (!aligned16(k) || !aligned16(v)) return DQK_ERR_INVALID;
+  if (batch <= 0 || ld_t <= 0 || hq <= 0 || hkv <= 0 || hq % hkv != 0) return DQK_ERR_INVALID;
+  if (!supported_dim(d) || !supported_group(hq, hkv)) return DQK_ERR_UNSUPPORTED;
+  if (!isfinite(sm_scale) || !valid_split(split)) return DQK_ERR_INVALID;
+  const size_t need = decode_ws_bytes(batch, hkv, hq, d, ld_t, split);
+  if (!workspace || ws_bytes < need || !aligned16(workspace)) return DQK_ERR_WORKSPACE;
+  return from_hip(dqk::launch_bf16_decode(q, k, v, lengths, batch, hq, hkv, d, ld_t, sm_scale,
+                                          pick_split(split), out, static_cast<float *>(workspace),
+                                          reinterpret_cast<hipStream_t>(stream)));
+}
+
+dqk_status dqk_debug_f16_from_f32(const float *x, uint16_t *out, size_t n, dqk_stream_t stream) {
+  if ((!x || !out) && n > 0) return DQK_ERR_INVALID;
+  return from_hip(dqk::launch_f16_convert(x, out, n, reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

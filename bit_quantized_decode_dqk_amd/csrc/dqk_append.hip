@@ -1,0 +1,203 @@
+// Append step: key transform, channel-0 protection, per-channel key groups,
+// per-token value groups, 2-bit packing -- fused in one kernel.
+//
+// Dual-QK (arXiv abstract; tech.dede.sh summary, "Paired transforms instead of
+// shared rotation" and "Throughput on SGLang"): new keys go through the key
+// transform k' = k B, keys and values are stored in 2 bits with an fp16 scale
+// per group of 32, and channel 0 of the key is protected (kept in fp16 here).
+//
+// One workgroup handles one 32-token key group of one (batch row, KV head):
+// the new tokens of that group are transformed (each output one fp32 FMA chain
+// over input channels in ascending order, so the result is reproducible bit for
+// bit), channel 0 goes to fp16, and either the group is complete -- then every
+// channel 1..d-1 is quantized over its 32 tokens and packed as 8 bytes -- or the
+// exact values go to the tail rows.  Value rows are quantized per token in
+// 32-channel groups; their codes are merged into the 16-token words of the
+// channel-blocked value plane.  Built with -ffp-contract=off.
+#include "dqk_internal.h"
+
+namespace dqk {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <int D>
+struct AppendSmem {
+  float kx[kGroup][D];   // new keys of the group (fp32)
+  float kp[kGroup][D];   // transformed keys
+  float vx[kGroup][D];   // new values (fp32)
+  float v2s[kGroup][D / kGroup];  // 2*scale per (token, value group)
+};
+
+__device__ __forceinline__ float load_in(const void *p, bool bf16, size_t i) {
+  return bf16 ? bf16_value(static_cast<const uint16_t *>(p)[i]) : static_cast<const float *>(p)[i];
+}
+
+template <int D>
+__device__ void store_group(const dqk_cache &c, int b, int g, int grp, int L, int n,
+                            const void *k_new, const void *v_new, bool bf16,
+                            const float *__restrict__ bmat, int max_new, AppendSmem<D> &sm) {
+  const int tid = threadIdx.x;
+  const int lo = max(L, grp * kGroup);
+  const int hi = min(L + n, grp * kGroup + kGroup);
+  const int cnt = hi - lo;                    // new tokens in this group, 1..32
+  const size_t unit = unit_index(c, b, g);
+  const size_t row0 = (unit * (size_t)max_new + (size_t)(lo - L)) * D;
+
+  for (int e = tid; e < cnt * D; e += kThreads) {
+    sm.kx[e / D][e % D] = load_in(k_new, bf16, row0 + e);
+    sm.vx[e / D][e % D] = load_in(v_new, bf16, row0 + e);
+  }
+  __syncthreads();
+
+  // k' = k B: thread owns output channel j for tokens r0, r0+S, ...
+  {
+    constexpr int S = kThreads / D;           // token slots per channel
+    constexpr int R = kGroup / S;             // tokens per thread
+    const int j = tid % D, r0 = tid / D;
+    const float *bcol = bmat + (size_t)g * D * D + j;
+    float acc[R];
+#pragma unroll
+    for (int m = 0; m < R; ++m) acc[m] = 0.0f;
+    for (int i = 0; i < D; ++i) {
+      const float bij = bcol[(size_t)i * D];
+#pragma unroll
+      for (int m = 0; m < R; ++m) acc[m] = __builtin_fmaf(sm.kx[r0 + m * S][i], bij, acc[m]);
+    }
+#pragma unroll
+    for (int m = 0; m < R; ++m)
+      if (r0 + m * S < cnt) sm.kp[r0 + m * S][j] = acc[m];
+  }
+  __syncthreads();
+
+  uint16_t *ch0 = c.k_ch0 + unit * (size_t)c.capacity;
+  for (int r = tid; r < cnt; r += kThreads) ch0[lo + r] = f16_bits(sm.kp[r][0]);
+
+  if (hi == grp * kGroup + kGroup) {
+    // The group is complete: quantize channels 1..D-1 over its 32 tokens.
+    const float *tail = c.k_tail + unit * (size_t)kGroup * D;
+    for (int ch = 1 + tid; ch < D; ch += kThreads) {
+      float x[kGroup];
+      float mx = 0.0f;
+#pragma unroll
+      for (int r = 0; r < kGroup; ++r) {
+        const int p = grp * kGroup + r;
+        x[r] = p < lo ? tail[(size_t)r * D + ch] : sm.kp[p - lo][ch];
+        mx = fmaxf(mx, fabsf(x[r]));
+      }
+      const uint16_t sb = f16_bits(mx / 3.0f);
+      const float two_s = 2.0f * f16_value(sb);
+      uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        w0 |= code_of(x[r], two_s) << (2 * r);
+        w1 |= code_of(x[r + 16], two_s) << (2 * r);
+      }
+      uint8_t *row = c.k_codes + (unit * D + ch) * (size_t)(c.capacity / 4);
+      *reinterpret_cast<uint2 *>(row + (size_t)grp * 8) = make_uint2(w0, w1);
+      c.k_scales[(unit * D + ch) * (size_t)(c.capacity / kGroup) + grp] = sb;
+    }
+  } else {
+    float *tail = c.k_tail + unit * (size_t)kGroup * D;
+    for (int e = tid; e < cnt * D; e += kThreads)
+      tail[(size_t)((lo + e / D) & 31) * D + e % D] = sm.kp[e / D][e % D];
+  }
+
+  // Value scales: one per (new token, 32-channel group).
+  constexpr int VG = D / kGroup;
+  uint16_t *vsc = c.v_scales + unit * (size_t)c.capacity * VG;
+  for (int e = tid; e < cnt * VG; e += kThreads) {
+    const int r = e / VG, jg = e % VG;
+    float mx = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i) mx = fmaxf(mx, fabsf(sm.vx[r][jg * kGroup + i]));
+    const uint16_t sb = f16_bits(mx / 3.0f);
+    vsc[(size_t)(lo + r) * VG + jg] = sb;
+    sm.v2s[r][jg] = 2.0f * f16_value(sb);
+  }
+  __syncthreads();
+
+  // Value codes: the group spans two 16-token words per channel.
+  uint32_t *vw = c.v_codes + unit * (size_t)(c.capacity / 16) * D;
+  for (int e = tid; e < 2 * D; e += kThreads) {
+    const int ch = e % D, half = e / D;
+    const int wlo = grp * kGroup + half * 16;
+    const int a = max(wlo, lo), z = min(wlo + 16, hi);
+    if (a >= z) continue;
+    uint32_t *wp = vw + (size_t)(wlo >> 4) * D + ch;
+    uint32_t w = *wp;
+    for (int p = a; p < z; ++p) {
+      const int sh = 2 * (p & 15);
+      const uint32_t u = code_of(sm.vx[p - lo][ch], sm.v2s[p - lo][ch / kGroup]);
+      w = (w & ~(3u << sh)) | (u << sh);
+    }
+    *wp = w;
+  }
+  __syncthreads();
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void append_kernel(dqk_cache c, const void *k_new,
+                                                          const void *v_new, int bf16,
+                                                          const float *__restrict__ bmat,
+                                                          const int32_t *__restrict__ n_new,
+                                                          int max_new, int blocks_per_unit) {
+  __shared__ AppendSmem<D> sm;
+  const int unit = blockIdx.x / blocks_per_unit;
+  const int bi = blockIdx.x % blocks_per_unit;
+  const int b = unit / c.num_kv_heads, g = unit % c.num_kv_heads;
+  const int L = c.lengths[b];
+  const int n = max(0, min(min(n_new[b], max_new), c.capacity - L));
+  if (n <= 0) return;
+  const int g0 = L / kGroup, g1 = (L + n - 1) / kGroup;
+  // The first group may read old tail rows while the last (unfinished) group
+  // writes tail rows; then one workgroup does both, first before last.
+  const bool merged = g1 > g0 && (L % kGroup) != 0 && ((L + n) % kGroup) != 0;
+  const int ngroups = g1 - g0 + 1;
+  if (bi >= ngroups) return;
+  if (merged && bi == ngroups - 1) return;
+  store_group<D>(c, b, g, g0 + bi, L, n, k_new, v_new, bf16 != 0, bmat, max_new, sm);
+  if (merged && bi == 0) store_group<D>(c, b, g, g1, L, n, k_new, v_new, bf16 != 0, bmat, max_new, sm);
+}
+
+__global__ void commit_lengths_kernel(int32_t *lengths, const int32_t *n_new, int batch,
+                                      int max_new, int cap) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= batch) return;
+  const int L = lengths[b];
+  const int n = max(0, min(min(n_new[b], max_new), cap - L));
+  lengths[b] = L + n;
+}
+
+__global__ void f16_convert_kernel(const float *x, uint16_t *out, size_t n) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = f16_bits(x[i]);
+}
+
+}  // namespace
+
+hipError_t launch_append(const dqk_cache &c, const void *k_new, const void *v_new, bool bf16,
+                         const float *bmat, const int32_t *n_new, int max_new, hipStream_t s) {
+  const int units = c.batch * c.num_kv_heads;
+  const int per_unit = (max_new + kGroup - 1) / kGroup + 1;  // a range can straddle one more group
+  const dim3 grid((unsigned)(units * per_unit));
+  if (c.head_dim == 64)
+    hipLaunchKernelGGL(append_kernel<64>, grid, dim3(kThreads), 0, s, c, k_new, v_new, (int)bf16,
+                       bmat, n_new, max_new, per_unit);
+  else
+    hipLaunchKernelGGL(append_kernel<128>, grid, dim3(kThreads), 0, s, c, k_new, v_new, (int)bf16,
+                       bmat, n_new, max_new, per_unit);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(commit_lengths_kernel, dim3((c.batch + 255) / 256), dim3(256), 0, s,
+                     c.lengths, n_new, c.batch, max_new, c.capacity);
+  return hipGetLastError();
+}
+
+hipError_t launch_f16_convert(const float *x, uint16_t *out, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(f16_convert_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, x, out, n);
+  return hipGetLastError();
+}
+
+}  // namespace dqk

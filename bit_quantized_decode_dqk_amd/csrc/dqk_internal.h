@@ -1,0 +1,65 @@
+// Internal declarations shared by the HIP sources of libdqk (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/dqk.h"
+
+namespace dqk {
+
+constexpr int kGroup = 32;          // tokens (keys) or channels (values) per scale
+constexpr int kDefaultSplit = 1024; // decode split length when the caller passes 0
+
+// fp32 -> binary16 bits: round to nearest even (the hardware conversion), with
+// subnormals, and finite values past the largest binary16 clamped to +-65504.
+__device__ __forceinline__ uint16_t f16_bits(float x) {
+  x = fminf(fmaxf(x, -65504.0f), 65504.0f);
+  _Float16 h = (_Float16)x;
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ float f16_value(uint16_t b) {
+  return (float)__builtin_bit_cast(_Float16, b);
+}
+
+__device__ __forceinline__ float bf16_value(uint16_t b) {
+  return __uint_as_float((uint32_t)b << 16);
+}
+
+// Code u of a 2-bit group with scale s stands for s*(2u-3).
+__device__ __forceinline__ float level_of(uint32_t u) { return (float)(int)(2u * u) - 3.0f; }
+
+// 2-bit code of x for the grid s*{-3,-1,1,3}: thresholds -2s, 0, 2s, ties upward.
+__device__ __forceinline__ uint32_t code_of(float x, float two_s) {
+  return (uint32_t)(x >= -two_s) + (uint32_t)(x >= 0.0f) + (uint32_t)(x >= two_s);
+}
+
+struct Shape {
+  int batch, hkv, d, cap;
+};
+
+// Element offsets of the planes for one unit (batch row b, KV head g).
+__host__ __device__ __forceinline__ size_t unit_index(const dqk_cache &c, int b, int g) {
+  return (size_t)b * c.num_kv_heads + g;
+}
+
+// Launchers (return the launch error, if any).
+hipError_t launch_append(const dqk_cache &c, const void *k_new, const void *v_new, bool bf16,
+                         const float *bmat, const int32_t *n_new, int max_new, hipStream_t s);
+hipError_t launch_select(const void *q, bool bf16, const float *amat, int batch, int hq, int hkv,
+                         int d, int keep, float *q_prime, int32_t *sel_idx, hipStream_t s);
+hipError_t launch_decode(const dqk_cache &c, const float *q_prime, const int32_t *sel_idx, int hq,
+                         int keep, float sm_scale, int split, float *out, float *ws,
+                         hipStream_t s);
+hipError_t launch_dequant(const dqk_cache &c, float *k_out, float *v_out, hipStream_t s);
+hipError_t launch_bf16_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                              const int32_t *lengths, int batch, int hq, int hkv, int d, int ld_t,
+                              float sm_scale, int split, float *out, float *ws, hipStream_t s);
+hipError_t launch_f16_convert(const float *x, uint16_t *out, size_t n, hipStream_t s);
+
+// Workspace: per work item (unit, split) and query head of its group: m, l, o[d].
+inline size_t partial_floats(int d) { return (size_t)d + 2; }
+inline int num_splits(int cap_tokens, int split) { return (cap_tokens + split - 1) / split; }
+
+}  // namespace dqk

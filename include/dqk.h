@@ -1,0 +1,167 @@
+/*
+ * dqk.h -- C ABI of the MI355X (gfx950) library for the Dual-QK decode step:
+ * single-token attention over a 2-bit KV cache whose keys and queries pass
+ * through paired transforms, reading only the key channels each query keeps.
+ *
+ * Source of the method: "Dual-QK: Sharp Queries and Flat Keys for Prunable
+ * 2-bit KV Caches" (arXiv abstract) and the tech.dede.sh summary of it, sections
+ * "Why the cache becomes a bottleneck", "Paired transforms instead of shared
+ * rotation", "Results at 128K context" and "Throughput on SGLang".  The pages
+ * fix the ingredients (paired non-orthogonal transforms, INT2 storage, channel-0
+ * protection, query-channel pruning at a given sparsity); the concrete formats
+ * and rules below are this library's definitions of them.
+ *
+ * Conventions for every call:
+ *  - Pointers are DEVICE pointers unless marked "host".  The caller owns all
+ *    memory; the library allocates nothing, keeps no pointer after returning
+ *    and holds no global state.  Calls are thread-safe.
+ *  - Work is enqueued on `stream` (0 = the null stream); no call synchronizes.
+ *  - Every argument the host can see is validated before anything is launched:
+ *    an invalid call returns an error status and launches nothing.  A launch
+ *    failure returns DQK_ERR_HIP.  Conditions only the device can see (the
+ *    contents of lengths/n_new/sel_idx, non-finite data) are preconditions; the
+ *    kernels clamp counts and indices so they never write out of bounds.
+ *
+ * Cache layout, version 1 (per batch row b and KV head g, "unit" = b*hkv + g):
+ *   k_codes  u8   [batch][hkv][d][cap/4]   key channel c, token t: byte t>>2 of the
+ *                                          channel's row, bits 2(t&3) (channel-major,
+ *                                          so a dropped channel is never read)
+ *   k_scales f16  [batch][hkv][d][cap/32]  scale of (channel c, tokens 32j..32j+31)
+ *   k_ch0    f16  [batch][hkv][cap]        key channel 0 of every token (protected)
+ *   k_tail   f32  [batch][hkv][32][d]      exact transformed keys of the unfinished
+ *                                          32-token group; row r valid for r < len%32
+ *   v_codes  u32  [batch][hkv][cap/16][d]  value token t, channel c: 32-bit word
+ *                                          (t>>4)*d + c, bits 2(t&15)
+ *   v_scales f16  [batch][hkv][cap][d/32]  scale of (token t, channels 32j..32j+31)
+ *   lengths  i32  [batch]                  tokens stored per row
+ * A 2-bit code u with scale s stands for s*(2u-3).  Rows of channel 0 in
+ * k_codes/k_scales exist but are never written or read.  Planes should be
+ * zero-filled before the first append for byte-reproducible contents.
+ */
+#ifndef DQK_H
+#define DQK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *dqk_stream_t; /* the same type as hipStream_t */
+
+typedef enum {
+    DQK_OK = 0,
+    DQK_ERR_INVALID = -1,     /* bad pointer, size, shape or count */
+    DQK_ERR_UNSUPPORTED = -2, /* valid in general, not built here (e.g. head_dim) */
+    DQK_ERR_WORKSPACE = -3,   /* workspace missing or too small */
+    DQK_ERR_HIP = -4          /* a HIP runtime call or launch failed */
+} dqk_status;
+
+typedef enum { DQK_F32 = 0, DQK_BF16 = 1 } dqk_dtype;
+
+typedef struct {
+    int32_t batch, num_kv_heads, head_dim, capacity; /* head_dim in {64, 128}; capacity % 32 == 0 */
+    uint8_t *k_codes;
+    uint16_t *k_scales;
+    uint16_t *k_ch0;
+    float *k_tail;
+    uint32_t *v_codes;
+    uint16_t *v_scales;
+    int32_t *lengths;
+} dqk_cache;
+
+/* Human-readable name of a status (static string). */
+const char *dqk_status_str(dqk_status s);
+
+/* Host query, no device work: byte sizes of the planes k_codes, k_scales, k_ch0,
+ * k_tail, v_codes, v_scales, lengths for the given shape (out_bytes: host [7]). */
+dqk_status dqk_cache_plane_bytes(int32_t batch, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t capacity, size_t *out_bytes);
+
+/* Append step ("every token adds new keys and values that must be kept for later
+ * attention steps"; key transform from "paired transforms"; 2-bit storage from
+ * "Quantization cuts storage to 2 bits per value"; channel-0 protection).
+ * For each batch row b, n = min(n_new[b], max_new, capacity - lengths[b]) tokens
+ * k_new[b][g][i][:], v_new[b][g][i][:] (i < n) are stored at positions
+ * lengths[b]..lengths[b]+n-1 of every KV head g, then lengths[b] += n:
+ *   k' = k B_g, one fp32 fused-multiply-add chain per output channel over input
+ *   channels in ascending order; k'_0 -> fp16 (round to nearest even, saturating
+ *   at +-65504); k' -> k_tail row p%32; when position p closes its 32-token group,
+ *   channels 1..d-1 of the group are quantized per channel; each value row is
+ *   quantized in groups of 32 channels.  Quantizer: s = fp16(max|x|/3),
+ *   u = [x >= -2s] + [x >= 0] + [x >= 2s].
+ * k_new, v_new: [batch][hkv][max_new][head_dim] of `dtype`; bmat: [hkv][d][d] fp32
+ * row-major; n_new: [batch] i32.  Launches two kernels (store, then lengths). */
+dqk_status dqk_transform_quantize_append(const dqk_cache *cache, const void *k_new,
+                                         const void *v_new, dqk_dtype dtype,
+                                         const float *bmat, const int32_t *n_new,
+                                         int32_t max_new, dqk_stream_t stream);
+
+/* Query transform and channel selection ("the query transform sharpens the
+ * distribution for pruning"; "dynamic channel pruning" at a query-channel
+ * sparsity).  For each (b, query head h), with KV head g = h / (hq/hkv):
+ * q' = q A_g (same FMA chain as above), written to q_prime; sel_idx receives, in
+ * ascending order, channel 0 plus the keep-1 channels c >= 1 of largest |q'_c|,
+ * equal magnitudes going to the lower index.
+ * q: [batch][hq][d] of `dtype`; amat: [hkv][d][d] fp32; q_prime: [batch][hq][d]
+ * fp32; sel_idx: [batch][hq][keep] i32; 1 <= keep <= d. */
+dqk_status dqk_select_channels(const void *q, dqk_dtype dtype, const float *amat,
+                               int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim,
+                               int32_t keep, float *q_prime, int32_t *sel_idx,
+                               dqk_stream_t stream);
+
+/* Host query: workspace bytes dqk_decode_attention needs for this cache shape,
+ * hq query heads and split length (split_tokens = 0: the library's choice). */
+dqk_status dqk_decode_workspace_bytes(const dqk_cache *cache, int32_t hq,
+                                      int32_t split_tokens, size_t *out_bytes);
+
+/* Decode attention over the stored cache ("pruning removes ... key channels from
+ * reads"; values are never pruned).  For each (b, h) with T = lengths[b]:
+ *   z_t = sm_scale * sum_{c in sel_idx[b][h]} q'_c k~_{t,c}
+ *   out[b][h] = sum_t softmax(z)_t v~_t        (T = 0 gives zeros)
+ * where k~ is channel 0's fp16 value, the 2-bit value of complete groups, or the
+ * exact tail.  Only the kept key channels' codes and scales are read from HBM.
+ * The sequence is split into chunks of split_tokens (a multiple of 32; 0 = the
+ * library's choice) reduced with an online-max combine.  fp32 accumulation.
+ * q_prime: [batch][hq][d] fp32; sel_idx: [batch][hq][keep] as produced by
+ * dqk_select_channels; out: [batch][hq][d] fp32; workspace: device scratch of at
+ * least dqk_decode_workspace_bytes (contents need no initialization). */
+dqk_status dqk_decode_attention(const dqk_cache *cache, const float *q_prime,
+                                const int32_t *sel_idx, int32_t hq, int32_t keep,
+                                float sm_scale, int32_t split_tokens, float *out,
+                                void *workspace, size_t workspace_bytes,
+                                dqk_stream_t stream);
+
+/* Dense dequantized cache for checking and inspection: k_out, v_out
+ * [batch][hkv][capacity][d] fp32 hold k~ and v~ as defined above for t < len and
+ * zero past it.  Not on the decode path. */
+dqk_status dqk_dequant_reference(const dqk_cache *cache, float *k_out, float *v_out,
+                                 dqk_stream_t stream);
+
+/* Unpruned BF16 decode, the comparison the pages measure against ("relative to
+ * unpruned BF16"): out[b][h] = softmax(sm_scale * q K^T) V over raw bf16 keys and
+ * values, no transforms, no quantization, fp32 accumulation.
+ * q: [batch][hq][d] bf16; k, v: [batch][hkv][ld_t][d] bf16 (token-major);
+ * lengths: [batch] i32 (<= ld_t); out: [batch][hq][d] fp32; workspace as for
+ * dqk_decode_attention, sized by dqk_bf16_decode_workspace_bytes. */
+dqk_status dqk_bf16_decode_workspace_bytes(int32_t batch, int32_t hq, int32_t hkv,
+                                           int32_t head_dim, int32_t ld_t,
+                                           int32_t split_tokens, size_t *out_bytes);
+dqk_status dqk_bf16_decode_attention(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                     const int32_t *lengths, int32_t batch, int32_t hq,
+                                     int32_t hkv, int32_t head_dim, int32_t ld_t,
+                                     float sm_scale, int32_t split_tokens, float *out,
+                                     void *workspace, size_t workspace_bytes,
+                                     dqk_stream_t stream);
+
+/* Diagnostic: the device's fp32 -> fp16 conversion used for every stored scale
+ * and channel-0 key (round to nearest even, subnormals kept, saturating at
+ * +-65504), element-wise over n values.  x: [n] fp32, out: [n] u16. */
+dqk_status dqk_debug_f16_from_f32(const float *x, uint16_t *out, size_t n,
+                                  dqk_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,146 @@
+"""CPU checks of the C ABI: the library loads, exports every declared entry point,
+and rejects invalid arguments on the host before any device work.  No call here
+reaches a kernel launch."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import bit_quantized_decode_dqk_amd as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dqk.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
+
+
+def declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dqk_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    L = M.lib()
+    names = declared()
+    assert "dqk_decode_attention" in names and "dqk_transform_quantize_append" in names
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(M.EXPORTS)
+
+
+def test_status_strings():
+    L = M.lib()
+    for s in (OK, INVALID, UNSUPPORTED, WORKSPACE, -4):
+        assert L.dqk_status_str(s)
+    assert L.dqk_status_str(OK) == b"ok"
+
+
+def test_plane_bytes():
+    assert M.cache_plane_bytes(1, 8, 128, 131104) == [
+        8 * 128 * 131104 // 4, 8 * 128 * (131104 // 32) * 2, 8 * 131104 * 2, 8 * 32 * 128 * 4,
+        8 * (131104 // 16) * 128 * 4, 8 * 131104 * 4 * 2, 4]
+    out = (C.c_size_t * 7)()
+    L = M.lib()
+    assert L.dqk_cache_plane_bytes(1, 1, 96, 64, out) == UNSUPPORTED
+    assert L.dqk_cache_plane_bytes(1, 1, 64, 48, out) == INVALID
+    assert L.dqk_cache_plane_bytes(0, 1, 64, 64, out) == INVALID
+    assert L.dqk_cache_plane_bytes(1, 1, 64, 64, None) == INVALID
+
+
+def fake_cache(**kw):
+    """A cache descriptor with aligned, non-null placeholder pointers."""
+    vals = dict(batch=2, num_kv_heads=2, head_dim=128, capacity=256)
+    vals.update({k: v for k, v in kw.items() if k in vals})
+    ptrs = {n: 0x10000 * (i + 1) for i, n in enumerate(M.PLANES)}
+    ptrs.update({k: v for k, v in kw.items() if k in ptrs})
+    return M._Cache(vals["batch"], vals["num_kv_heads"], vals["head_dim"], vals["capacity"],
+                    *(ptrs[n] for n in M.PLANES))
+
+
+def test_cache_validation_without_gpu():
+    L = M.lib()
+    out = C.c_size_t(0)
+    assert L.dqk_decode_workspace_bytes(C.byref(fake_cache()), 8, 0, C.byref(out)) == OK
+    assert out.value == 2 * 2 * 1 * 4 * 130 * 4          # 1 split of 1024 covers 256 tokens
+    assert L.dqk_decode_workspace_bytes(C.byref(fake_cache()), 8, 64, C.byref(out)) == OK
+    assert out.value == 2 * 2 * 4 * 4 * 130 * 4
+    for bad in (dict(capacity=100), dict(batch=0), dict(k_codes=0), dict(v_codes=0x10004),
+                dict(lengths=0)):
+        assert L.dqk_decode_workspace_bytes(C.byref(fake_cache(**bad)), 8, 0, C.byref(out)) == INVALID
+    assert L.dqk_decode_workspace_bytes(C.byref(fake_cache(head_dim=96)), 8, 0, C.byref(out)) == UNSUPPORTED
+    assert L.dqk_decode_workspace_bytes(C.byref(fake_cache()), 6, 0, C.byref(out)) == UNSUPPORTED
+    assert L.dqk_decode_workspace_bytes(C.byref(fake_cache()), 8, 48, C.byref(out)) == INVALID
+    assert L.dqk_decode_workspace_bytes(None, 8, 0, C.byref(out)) == INVALID
+
+
+def test_decode_validation_without_gpu():
+    L = M.lib()
+    c = C.byref(fake_cache())
+    q, idx, out, ws = 0x20000, 0x30000, 0x40000, 0x50000
+    big = 1 << 30
+    assert L.dqk_decode_attention(c, None, idx, 8, 77, 0.1, 0, out, ws, big, None) == INVALID
+    assert L.dqk_decode_attention(c, q, idx, 8, 0, 0.1, 0, out, ws, big, None) == INVALID
+    assert L.dqk_decode_attention(c, q, idx, 8, 129, 0.1, 0, out, ws, big, None) == INVALID
+    assert L.dqk_decode_attention(c, q, idx, 7, 77, 0.1, 0, out, ws, big, None) == INVALID
+    assert L.dqk_decode_attention(c, q, idx, 6, 77, 0.1, 0, out, ws, big, None) == UNSUPPORTED
+    assert L.dqk_decode_attention(c, q, idx, 8, 77, float("nan"), 0, out, ws, big, None) == INVALID
+    assert L.dqk_decode_attention(c, q, idx, 8, 77, 0.1, 33, out, ws, big, None) == INVALID
+    assert L.dqk_decode_attention(c, q, idx, 8, 77, 0.1, 0, out, None, big, None) == WORKSPACE
+    assert L.dqk_decode_attention(c, q, idx, 8, 77, 0.1, 0, out, ws, 16, None) == WORKSPACE
+    assert L.dqk_decode_attention(c, q, idx, 8, 77, 0.1, 0, out, ws + 4, big, None) == WORKSPACE
+
+
+def test_append_select_dequant_validation_without_gpu():
+    L = M.lib()
+    c = C.byref(fake_cache())
+    k, v, b, n = 0x20000, 0x30000, 0x40000, 0x50000
+    assert L.dqk_transform_quantize_append(c, None, v, 1, b, n, 4, None) == INVALID
+    assert L.dqk_transform_quantize_append(c, k, v, 7, b, n, 4, None) == INVALID
+    assert L.dqk_transform_quantize_append(c, k, v, 1, b, None, 4, None) == INVALID
+    assert L.dqk_transform_quantize_append(c, k, v, 1, b, n, -1, None) == INVALID
+    assert L.dqk_transform_quantize_append(c, k, v, 1, b, n, 257, None) == INVALID
+    assert L.dqk_transform_quantize_append(c, k, v, 1, b, n, 0, None) == OK   # nothing to do
+    assert L.dqk_transform_quantize_append(C.byref(fake_cache(head_dim=256)), k, v, 1, b, n, 4,
+                                           None) == UNSUPPORTED
+    q, a, qp, idx = 0x20000, 0x30000, 0x40000, 0x50000
+    assert L.dqk_select_channels(q, 1, a, 2, 8, 2, 128, 0, qp, idx, None) == INVALID
+    assert L.dqk_select_channels(q, 1, a, 2, 8, 2, 128, 129, qp, idx, None) == INVALID
+    assert L.dqk_select_channels(q, 1, a, 2, 8, 3, 128, 77, qp, idx, None) == INVALID
+    assert L.dqk_select_channels(q, 1, a, 2, 8, 2, 80, 77, qp, idx, None) == UNSUPPORTED
+    assert L.dqk_select_channels(None, 1, a, 2, 8, 2, 128, 77, qp, idx, None) == INVALID
+    assert L.dqk_dequant_reference(c, None, 0x20000, None) == INVALID
+    assert L.dqk_dequant_reference(C.byref(fake_cache(capacity=0)), 0x10, 0x20, None) == INVALID
+
+
+def test_bf16_decode_validation_without_gpu():
+    L = M.lib()
+    out = C.c_size_t(0)
+    assert L.dqk_bf16_decode_workspace_bytes(1, 32, 8, 128, 131072, 0, C.byref(out)) == OK
+    assert out.value == 8 * 128 * 4 * 130 * 4
+    assert L.dqk_bf16_decode_workspace_bytes(1, 32, 8, 96, 1024, 0, C.byref(out)) == UNSUPPORTED
+    args = [0x20000, 0x30000, 0x40000, 0x50000, 1, 32, 8, 128, 1024, 0.1, 0, 0x60000, 0x70000,
+            1 << 30, None]
+    bad = list(args)
+    bad[1] = 0x30004                      # misaligned keys
+    assert L.dqk_bf16_decode_attention(*bad) == INVALID
+    bad = list(args)
+    bad[12] = None
+    assert L.dqk_bf16_decode_attention(*bad) == WORKSPACE
+    bad = list(args)
+    bad[5] = 24
+    assert L.dqk_bf16_decode_attention(*bad) == UNSUPPORTED
+
+
+def test_keep_count_matches_oracle(orc):
+    for d in (64, 128):
+        for s in range(0, 101):
+            assert M.keep_for_sparsity(d, s) == orc.keep_count(d, s)
+
+
+def test_binding_raises_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(M, "_lib", None)
+    monkeypatch.setattr(M, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(M.DqkError):
+        M.lib()

@@ -1,0 +1,257 @@
+"""GPU parity: the HIP library through its C ABI against the CPU oracle.
+
+Bit-exact: cache planes (codes, scales, channel 0, tail), q', selected channel
+sets, the dense dequantized cache, the fp16 conversion.  Within 2e-3 (max over
+heads of ||o - o_ref||_inf / ||o_ref||_inf): attention outputs.  Inputs are the
+seeded synthetic workloads, at sizes the oracle finishes in seconds that still
+span several splits and a ragged tail.
+"""
+import numpy as np
+import pytest
+
+import bit_quantized_decode_dqk_amd as M
+import workloads as W
+from gpu_util import (REL_TOL, assert_same_cache, dev_f32, dev_i32, dev_input, planes_np,
+                      rel_err, say)
+
+pytestmark = pytest.mark.gpu
+
+
+def _counts(wl, pos, n):
+    return np.clip(np.array(wl.ctx) - pos, 0, n).astype(np.int32)
+
+
+def build_gpu(wl, chunks=None, kv=None):
+    a, b = W.transforms(wl)
+    k, v = kv if kv is not None else W.prefill_kv(wl)
+    cache = M.Cache(wl.batch, wl.hkv, wl.d, wl.cap)
+    bm = dev_f32(b)
+    chunks = chunks or [max(wl.ctx)]
+    pos = 0
+    for n in chunks:
+        n = min(n, wl.cap - pos)
+        if n <= 0:
+            break
+        M.transform_quantize_append(cache, dev_input(k[:, :, pos:pos + n], wl.dtype),
+                                    dev_input(v[:, :, pos:pos + n], wl.dtype), bm,
+                                    dev_i32(_counts(wl, pos, n)))
+        pos += n
+    return cache, a, b, k, v
+
+
+def build_oracle(orc, wl, k, v, b):
+    c = orc.Cache(wl.batch, wl.hkv, wl.d, wl.cap)
+    n = max(wl.ctx)
+    c.append(k[:, :, :n], v[:, :, :n], b, list(wl.ctx))
+    return c
+
+
+def gpu_queries(wl, q, a, keep):
+    qp, idx = M.select_channels(dev_input(q, wl.dtype), dev_f32(a), wl.hkv, keep)
+    return qp, idx
+
+
+# ----------------------------------------------------------------------------- conversion
+
+def test_f16_conversion_matches_oracle(orc):
+    """Every positive pattern with biased exponent 100..143, both signs of a
+    stride through it, zeros/infinities, and random patterns."""
+    say("f16 conversion: exponents 100..143")
+    lo, hi = 100 << 23, 144 << 23
+    step = 1 << 26
+    for start in range(lo, hi, step):
+        bits = np.arange(start, min(start + step, hi), dtype=np.uint32)
+        x = bits.view(np.float32)
+        got = M.debug_f16_from_f32(dev_f32(x)).cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, orc.f16_from_f32(x)), hex(start)
+    rnd = np.random.default_rng(5).integers(0, 1 << 32, size=1 << 22, dtype=np.uint64).astype(np.uint32)
+    x = rnd.view(np.float32)
+    x = x[~np.isnan(x)]
+    neg = np.arange(lo, hi, 997, dtype=np.uint32) | np.uint32(0x80000000)
+    x = np.concatenate([x, neg.view(np.float32),
+                        np.array([0.0, -0.0, np.inf, -np.inf], dtype=np.float32)])
+    got = M.debug_f16_from_f32(dev_f32(x)).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, orc.f16_from_f32(x))
+
+
+# ----------------------------------------------------------------------------- append
+
+def test_append_tiny_bulk_single_and_mixed(orc):
+    wl = W.workload("tiny")
+    say("append tiny bulk")
+    g_bulk, a, b, k, v = build_gpu(wl)
+    ref = build_oracle(orc, wl, k, v, b)
+    assert_same_cache(planes_np(g_bulk), ref)
+    say("append tiny single-token x1024")
+    g_one, *_ = build_gpu(wl, [1] * 1024, kv=(k, v))
+    assert_same_cache(planes_np(g_one), ref)
+    say("append tiny mixed chunks")
+    g_mix, *_ = build_gpu(wl, [31, 1, 33, 2, 100, 64, 17, 16, 760], kv=(k, v))
+    assert_same_cache(planes_np(g_mix), ref)
+
+
+@pytest.mark.parametrize("chunks", [[1000], [500, 500], [31, 200, 769], [1] * 70 + [930]])
+def test_append_gqa_ragged(orc, chunks):
+    wl = W.custom("ragged-append", 21, 3, 32, 8, 128, [1000, 33, 31], 1024, "bf16",
+                  log_uniform_key_scales=True)
+    say("append ragged", chunks[:3])
+    g, a, b, k, v = build_gpu(wl, chunks)
+    ref = build_oracle(orc, wl, k, v, b)
+    assert_same_cache(planes_np(g), ref)
+
+
+def test_append_head_dim_64_and_capacity_clamp(orc):
+    wl = W.custom("d64", 22, 2, 4, 2, 64, [96, 64], 96, "f32", random_outlier_channels=3)
+    g, a, b, k, v = build_gpu(wl)
+    ref = build_oracle(orc, wl, k, v, b)
+    assert_same_cache(planes_np(g), ref)
+    # appending past capacity is clamped on both sides
+    extra = np.random.default_rng(1).standard_normal((2, 2, 40, 64)).astype(np.float32)
+    M.transform_quantize_append(g, dev_f32(extra), dev_f32(extra), dev_f32(b), dev_i32([40, 40]))
+    ref.append(extra, extra, b, [40, 40])
+    assert list(ref.lengths) == [96, 96]
+    assert_same_cache(planes_np(g), ref)
+
+
+def test_dequant_matches_oracle(orc):
+    wl = W.custom("dq", 23, 2, 8, 2, 128, [300, 77], 320, "bf16", log_uniform_key_scales=True)
+    g, a, b, k, v = build_gpu(wl)
+    ref = build_oracle(orc, wl, k, v, b)
+    kg, vg = M.dequant_reference(g)
+    ko, vo = ref.dequant()
+    assert np.array_equal(kg.cpu().numpy(), ko)
+    assert np.array_equal(vg.cpu().numpy(), vo)
+
+
+# ----------------------------------------------------------------------------- select
+
+@pytest.mark.parametrize("name", W.WORKLOADS)
+def test_select_matches_oracle(orc, name):
+    wl = W.workload(name)
+    a, _ = W.transforms(wl)
+    q = W.queries(wl)
+    for keep in sorted({1, 2, orc.keep_count(wl.d, 60), orc.keep_count(wl.d, 40), wl.d - 1, wl.d}):
+        qp, idx = gpu_queries(wl, q, a, keep)
+        qpo, idxo = orc.queries(q, a, wl.hkv, keep)
+        assert np.array_equal(qp.cpu().numpy().view(np.uint32), qpo.view(np.uint32)), keep
+        assert np.array_equal(idx.cpu().numpy(), idxo), keep
+
+
+def test_select_forced_ties(orc):
+    """Duplicated, negated and signed-zero query channels: ties go to lower index."""
+    d, hq = 128, 8
+    rng = np.random.default_rng(30)
+    q = rng.choice(np.array([0.0, -0.0, 1.0, -1.0, 2.5, -2.5], dtype=np.float32), (2, hq, d))
+    eye = np.stack([np.eye(d, dtype=np.float32)] * 2)
+    for keep in (1, 20, 77, 128):
+        qp, idx = M.select_channels(dev_f32(q), dev_f32(eye), 2, keep)
+        qpo, idxo = orc.queries(q, eye, 2, keep)
+        assert np.array_equal(idx.cpu().numpy(), idxo)
+        assert np.array_equal(qp.cpu().numpy().view(np.uint32), qpo.view(np.uint32))
+
+
+# ----------------------------------------------------------------------------- decode
+
+def decode_case(orc, wl, sparsity=40, sm_mult=1.0, splits=(0,), step=0):
+    say("decode", wl.describe(), "s", sparsity, "sm x", sm_mult, "splits", splits)
+    g, a, b, k, v = build_gpu(wl)
+    ref = build_oracle(orc, wl, k, v, b)
+    keep = orc.keep_count(wl.d, sparsity)
+    q = W.queries(wl, step)
+    qp, idx = gpu_queries(wl, q, a, keep)
+    qpo, idxo = orc.queries(q, a, wl.hkv, keep)
+    assert np.array_equal(idx.cpu().numpy(), idxo)
+    sm = W.default_sm_scale(wl.d) * sm_mult
+    o_ref = ref.decode(qpo, idxo, sm)
+    outs = []
+    for sp in splits:
+        out = M.decode_attention(g, qp, idx, sm, split_tokens=sp).cpu().numpy()
+        err = rel_err(out, o_ref)
+        say(f"  split {sp}: max rel err {err:.3e}")
+        assert err <= REL_TOL, (sp, err)
+        outs.append(out)
+    return g, outs, o_ref
+
+
+def test_decode_tiny_full(orc):
+    decode_case(orc, W.workload("tiny"), splits=(0, 32, 256, 1024))
+    decode_case(orc, W.workload("tiny"), sm_mult=0.05, splits=(0, 96))
+
+
+def test_decode_gqa_reduced(orc):
+    wl = W.workload("gqa8k", batch=2, ctx=2500)
+    decode_case(orc, wl, splits=(0, 64, 1024, 4096))
+    decode_case(orc, wl, sm_mult=0.01, splits=(0, 352))
+    decode_case(orc, wl, sparsity=0)
+    decode_case(orc, wl, sparsity=60, sm_mult=0.02)
+
+
+def test_decode_ragged_edges(orc):
+    """Lengths 0, 1, 31, 32, 33, 64 and 95 in one batch (empty rows give zeros)."""
+    wl = W.custom("edges", 24, 7, 16, 8, 128, [0, 1, 31, 32, 33, 64, 95], 96, "bf16",
+                  log_uniform_key_scales=True)
+    g, outs, o_ref = decode_case(orc, wl, splits=(0, 32, 64))
+    for out in outs:
+        assert not out[0].any()
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(1, 1, 64), (2, 1, 64), (8, 1, 64), (4, 2, 128),
+                                      (16, 2, 128), (64, 8, 128)])
+def test_decode_group_sizes(orc, hq, hkv, d):
+    wl = W.custom(f"g{hq}-{hkv}-{d}", 25, 2, hq, hkv, d, [700, 1333], 1344, "bf16",
+                  log_uniform_key_scales=True, student_t_queries=(hq == 64))
+    decode_case(orc, wl, splits=(0, 128))
+    decode_case(orc, wl, sm_mult=0.02, splits=(0,))
+
+
+def test_decode_poisoned_dropped_channels(orc):
+    """Codes and scales of channels no head of the group keeps are overwritten
+    with 0xFF / fp16 NaN: the output is bitwise unchanged, so they are never used."""
+    wl = W.workload("gqa8k", batch=2, ctx=1500)
+    g, a, b, k, v = build_gpu(wl)
+    keep = orc.keep_count(wl.d, 60)
+    qp, idx = gpu_queries(wl, W.queries(wl), a, keep)
+    sm = W.default_sm_scale(wl.d) * 0.02
+    base = M.decode_attention(g, qp, idx, sm).cpu().numpy()
+    idx_np = idx.cpu().numpy()
+    poisoned = 0
+    for bb in range(wl.batch):
+        for gg in range(wl.hkv):
+            kept = set(idx_np[bb, gg * wl.group:(gg + 1) * wl.group].ravel().tolist())
+            drop = [c for c in range(1, wl.d) if c not in kept]
+            poisoned += len(drop)
+            if drop:
+                g.k_codes[bb, gg, drop] = 0xFF
+                g.k_scales[bb, gg, drop] = 0x7E00     # fp16 NaN bits
+    assert poisoned > 0
+    again = M.decode_attention(g, qp, idx, sm).cpu().numpy()
+    assert np.array_equal(base.view(np.uint32), again.view(np.uint32))
+
+
+def test_decode_deterministic(orc):
+    wl = W.workload("gqa8k", batch=1, ctx=3000)
+    g, a, b, k, v = build_gpu(wl)
+    qp, idx = gpu_queries(wl, W.queries(wl), a, 77)
+    o1 = M.decode_attention(g, qp, idx, 0.01).cpu().numpy()
+    o2 = M.decode_attention(g, qp, idx, 0.01).cpu().numpy()
+    assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
+
+
+# ----------------------------------------------------------------------------- bf16 comparator
+
+@pytest.mark.parametrize("lens,sm_mult", [([4096], 1.0), ([4096], 0.02), ([1000, 1, 0, 2049], 0.05)])
+def test_bf16_decode_matches_plain_attention(orc, lens, sm_mult):
+    wl = W.custom("bf16cmp", 26, len(lens), 32, 8, 128, lens, 4096 + 64, "bf16",
+                  log_uniform_key_scales=True)
+    say("bf16 decode", lens)
+    k, v = W.prefill_kv(wl)
+    q = W.queries(wl)
+    sm = W.default_sm_scale(wl.d) * sm_mult
+    ref = orc.plain_attention(q, k, v, list(wl.ctx), sm)
+    for sp in (0, 64, 2048):
+        out = M.bf16_decode_attention(dev_input(q, "bf16"), dev_input(k, "bf16"),
+                                      dev_input(v, "bf16"), dev_i32(wl.ctx), sm,
+                                      split_tokens=sp).cpu().numpy()
+        err = rel_err(out, ref)
+        say(f"  split {sp}: {err:.3e}")
+        assert err <= REL_TOL
