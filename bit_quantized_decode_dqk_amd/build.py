@@ -28,6 +28,7 @@ SOURCES = {
     "dqk_dequant.hip": ["-ffp-contract=off"],
     "dqk_decode.hip": [],
     "dqk_bf16.hip": [],
+    "dqk_combine.hip": [],
 }
 
 COMMON = ["-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -43,9 +43,20 @@ int pick_split(int split) { return split == 0 ? kDefaultSplit : split; }
 
 bool valid_split(int split) { return split == 0 || (split >= kGroup && split % kGroup == 0); }
 
-size_t decode_ws_bytes(int batch, int hkv, int hq, int d, int tokens, int split) {
-  const int nsplit = dqk::num_splits(tokens, pick_split(split));
+size_t ws_bytes_for(int batch, int hkv, int hq, int d, int tokens, int split) {
+  const int nsplit = dqk::num_splits(tokens, split);
   return (size_t)batch * hkv * nsplit * (size_t)(hq / hkv) * dqk::partial_floats(d) * sizeof(float);
+}
+
+// Split of the 2-bit decode: the caller's, else the library's default.
+int decode_split(const dqk_cache *c, int hq, int split) {
+  const int group = hq / c->num_kv_heads;
+  return split != 0 ? split
+                    : dqk::default_decode_split(group, c->capacity, c->batch * c->num_kv_heads);
+}
+
+bool valid_decode_split(int hq, int hkv, int split) {
+  return valid_split(split) && split <= dqk::max_split_tokens(hq / hkv);
 }
 
 }  // namespace
@@ -98,7 +109,7 @@ dqk_status dqk_select_channels(const void *q, dqk_dtype dtype, const float *amat
   if (!q || !amat || !q_prime || !sel_idx) return DQK_ERR_INVALID;
   if (dtype != DQK_F32 && dtype != DQK_BF16) return DQK_ERR_INVALID;
   if (batch <= 0 || hq <= 0 || hkv <= 0 || hq % hkv != 0) return DQK_ERR_INVALID;
-  if (!supported_dim(d)) return DQK_ERR_UNSUPPORTED;
+  if (!supported_dim(d) || !supported_group(hq, hkv)) return DQK_ERR_UNSUPPORTED;
   if (keep < 1 || keep > d) return DQK_ERR_INVALID;
   if ((int64_t)batch * hq > (1 << 30)) return DQK_ERR_INVALID;
   return from_hip(dqk::launch_select(q, dtype == DQK_BF16, amat, batch, hq, hkv, d, keep, q_prime,
@@ -111,9 +122,9 @@ dqk_status dqk_decode_workspace_bytes(const dqk_cache *cache, int32_t hq, int32_
   dqk_status st = check_cache(cache);
   if (st != DQK_OK) return st;
   if (!supported_group(hq, cache->num_kv_heads)) return DQK_ERR_UNSUPPORTED;
-  if (!valid_split(split)) return DQK_ERR_INVALID;
-  *out = decode_ws_bytes(cache->batch, cache->num_kv_heads, hq, cache->head_dim, cache->capacity,
-                         split);
+  if (!valid_decode_split(hq, cache->num_kv_heads, split)) return DQK_ERR_INVALID;
+  *out = ws_bytes_for(cache->batch, cache->num_kv_heads, hq, cache->head_dim, cache->capacity,
+                      decode_split(cache, hq, split));
   return DQK_OK;
 }
 
@@ -130,12 +141,13 @@ dqk_status dqk_decode_attention(const dqk_cache *cache, const float *q_prime,
   }
   if (keep < 1 || keep > cache->head_dim) return DQK_ERR_INVALID;
   if (!isfinite(sm_scale)) return DQK_ERR_INVALID;
-  if (!valid_split(split)) return DQK_ERR_INVALID;
-  const size_t need = decode_ws_bytes(cache->batch, cache->num_kv_heads, hq, cache->head_dim,
-                                      cache->capacity, split);
+  if (!valid_decode_split(hq, cache->num_kv_heads, split)) return DQK_ERR_INVALID;
+  const int sp = decode_split(cache, hq, split);
+  const size_t need = ws_bytes_for(cache->batch, cache->num_kv_heads, hq, cache->head_dim,
+                                   cache->capacity, sp);
   if (!workspace || ws_bytes < need || !aligned16(workspace)) return DQK_ERR_WORKSPACE;
-  return from_hip(dqk::launch_decode(*cache, q_prime, sel_idx, hq, keep, sm_scale,
-                                     pick_split(split), out, static_cast<float *>(workspace),
+  return from_hip(dqk::launch_decode(*cache, q_prime, sel_idx, hq, keep, sm_scale, sp, out,
+                                     static_cast<float *>(workspace),
                                      reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -153,7 +165,7 @@ dqk_status dqk_bf16_decode_workspace_bytes(int32_t batch, int32_t hq, int32_t hk
   if (!supported_dim(d)) return DQK_ERR_UNSUPPORTED;
   if (!supported_group(hq, hkv)) return DQK_ERR_UNSUPPORTED;
   if (!valid_split(split)) return DQK_ERR_INVALID;
-  *out = decode_ws_bytes(batch, hkv, hq, d, ld_t, split);
+  *out = ws_bytes_for(batch, hkv, hq, d, ld_t, pick_split(split));
   return DQK_OK;
 }
 
@@ -167,7 +179,7 @@ dqk_status dqk_bf16_decode_attention(const uint16_t *q, const uint16_t *k, const
   if (batch <= 0 || ld_t <= 0 || hq <= 0 || hkv <= 0 || hq % hkv != 0) return DQK_ERR_INVALID;
   if (!supported_dim(d) || !supported_group(hq, hkv)) return DQK_ERR_UNSUPPORTED;
   if (!isfinite(sm_scale) || !valid_split(split)) return DQK_ERR_INVALID;
-  const size_t need = decode_ws_bytes(batch, hkv, hq, d, ld_t, split);
+  const size_t need = ws_bytes_for(batch, hkv, hq, d, ld_t, pick_split(split));
   if (!workspace || ws_bytes < need || !aligned16(workspace)) return DQK_ERR_WORKSPACE;
   return from_hip(dqk::launch_bf16_decode(q, k, v, lengths, batch, hq, hkv, d, ld_t, sm_scale,
                                           pick_split(split), out, static_cast<float *>(workspace),

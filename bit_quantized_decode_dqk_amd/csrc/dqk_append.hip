@@ -50,23 +50,42 @@ __device__ void store_group(const dqk_cache &c, int b, int g, int grp, int L, in
   }
   __syncthreads();
 
-  // k' = k B: thread owns output channel j for tokens r0, r0+S, ...
+  // k' = k B: thread owns output channel j for tokens r0, r0+S, ...; rows of B
+  // are fetched kBRows at a time so that many loads are in flight.
   {
     constexpr int S = kThreads / D;           // token slots per channel
-    constexpr int R = kGroup / S;             // tokens per thread
+    constexpr int R = kGroup / S;             // tokens per thread at most
+    constexpr int kBRows = 16;
     const int j = tid % D, r0 = tid / D;
     const float *bcol = bmat + (size_t)g * D * D + j;
-    float acc[R];
+    if (cnt <= S) {                            // decode-step appends: one token per thread
+      float acc = 0.0f;
+      for (int i0 = 0; i0 < D; i0 += kBRows) {
+        float bv[kBRows];
 #pragma unroll
-    for (int m = 0; m < R; ++m) acc[m] = 0.0f;
-    for (int i = 0; i < D; ++i) {
-      const float bij = bcol[(size_t)i * D];
+        for (int r = 0; r < kBRows; ++r) bv[r] = bcol[(size_t)(i0 + r) * D];
 #pragma unroll
-      for (int m = 0; m < R; ++m) acc[m] = __builtin_fmaf(sm.kx[r0 + m * S][i], bij, acc[m]);
+        for (int r = 0; r < kBRows; ++r) acc = __builtin_fmaf(sm.kx[r0][i0 + r], bv[r], acc);
+      }
+      if (r0 < cnt) sm.kp[r0][j] = acc;
+    } else {
+      float acc[R];
+#pragma unroll
+      for (int m = 0; m < R; ++m) acc[m] = 0.0f;
+      for (int i0 = 0; i0 < D; i0 += kBRows) {
+        float bv[kBRows];
+#pragma unroll
+        for (int r = 0; r < kBRows; ++r) bv[r] = bcol[(size_t)(i0 + r) * D];
+#pragma unroll
+        for (int r = 0; r < kBRows; ++r)
+#pragma unroll
+          for (int m = 0; m < R; ++m)
+            acc[m] = __builtin_fmaf(sm.kx[r0 + m * S][i0 + r], bv[r], acc[m]);
+      }
+#pragma unroll
+      for (int m = 0; m < R; ++m)
+        if (r0 + m * S < cnt) sm.kp[r0 + m * S][j] = acc[m];
     }
-#pragma unroll
-    for (int m = 0; m < R; ++m)
-      if (r0 + m * S < cnt) sm.kp[r0 + m * S][j] = acc[m];
   }
   __syncthreads();
 

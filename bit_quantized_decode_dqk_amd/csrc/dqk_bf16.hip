@@ -45,9 +45,9 @@ __global__ __launch_bounds__(kThreads) void bf16_decode_kernel(
   const int len = max(0, min(lengths[b], ld_t));
   const int t_begin = s * split;
   const int t_end = min(t_begin + split, len);
-  float *wsp = ws + (size_t)item * G * (D + 2);
+  float *wsp = ws + (size_t)item * G * (D + kPartialHead);
   if (t_begin >= t_end) {
-    for (int e = tid; e < G * (D + 2); e += kThreads) wsp[e] = (e % (D + 2) == 0) ? -INFINITY : 0.0f;
+    for (int e = tid; e < G * (D + kPartialHead); e += kThreads) wsp[e] = (e % (D + kPartialHead) == 0) ? -INFINITY : 0.0f;
     return;
   }
   for (int e = tid; e < G * D; e += kThreads)
@@ -133,39 +133,13 @@ __global__ __launch_bounds__(kThreads) void bf16_decode_kernel(
       float o = 0.0f;
 #pragma unroll
       for (int pp = 0; pp < PARTS; ++pp) o += red[((size_t)pp * G + h) * D + tid];
-      wsp[h * (D + 2) + 2 + tid] = o;
+      wsp[h * (D + kPartialHead) + kPartialHead + tid] = o;
       if (tid == 0) {
-        wsp[h * (D + 2) + 0] = sm.mrun[h];
-        wsp[h * (D + 2) + 1] = sm.lrun[h];
+        wsp[h * (D + kPartialHead) + 0] = sm.mrun[h];
+        wsp[h * (D + kPartialHead) + 1] = sm.lrun[h];
       }
     }
   }
-}
-
-// Same combine as the 2-bit decode (partials m, l, o[d] per split and head).
-template <int D>
-__global__ __launch_bounds__(D) void bf16_combine_kernel(const float *__restrict__ ws, int hq,
-                                                         int hkv, int nsplit, float *__restrict__ out) {
-  const int row = blockIdx.x;
-  const int b = row / hq, h = row % hq;
-  const int G = hq / hkv;
-  const int unit = b * hkv + h / G, hi = h % G;
-  const int c = threadIdx.x;
-  const float *base = ws + ((size_t)unit * nsplit * G + hi) * (D + 2);
-  const size_t stride = (size_t)G * (D + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s)
-    if (base[s * stride + 1] > 0.0f) M = fmaxf(M, base[s * stride]);
-  float den = 0.0f, acc = 0.0f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float *p = base + s * stride;
-    if (p[1] > 0.0f) {
-      const float f = exp2f(p[0] - M);
-      den = fmaf(p[1], f, den);
-      acc = fmaf(p[2 + c], f, acc);
-    }
-  }
-  out[(size_t)row * D + c] = den > 0.0f ? acc / den : 0.0f;
 }
 
 template <int D, int G>
@@ -178,9 +152,7 @@ hipError_t launch_t(const uint16_t *q, const uint16_t *k, const uint16_t *v, con
                      v, lengths, hq, hkv, ld_t, scale2, split, nsplit, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bf16_combine_kernel<D>, dim3((unsigned)(batch * hq)), dim3(D), 0, s, ws, hq,
-                     hkv, nsplit, out);
-  return hipGetLastError();
+  return launch_combine(ws, batch, hq, hkv, D, nsplit, out, s);
 }
 
 template <int D>

@@ -9,7 +9,21 @@
 namespace dqk {
 
 constexpr int kGroup = 32;          // tokens (keys) or channels (values) per scale
-constexpr int kDefaultSplit = 1024; // decode split length when the caller passes 0
+constexpr int kDefaultSplit = 1024; // bf16 decode split length when the caller passes 0
+
+// 2-bit decode: a split's logits live in LDS, G * split <= kMaxSplitTokensTimesG.
+constexpr int kMaxSplitTokensTimesG = 8192;
+inline int max_split_tokens(int group) { return kMaxSplitTokensTimesG / group; }
+
+// Default 2-bit decode split: aim at >= 512 work items (two per compute unit),
+// in 256-token steps, at most the LDS bound.
+inline int default_decode_split(int group, int capacity, int units) {
+  const long long per = ((long long)capacity * units + 511) / 512;
+  int s = (int)((per + 255) / 256 * 256);
+  if (s < 256) s = 256;
+  const int mx = max_split_tokens(group);
+  return s > mx ? mx : s;
+}
 
 // fp32 -> binary16 bits: round to nearest even (the hardware conversion), with
 // subnormals, and finite values past the largest binary16 clamped to +-65504.
@@ -56,10 +70,14 @@ hipError_t launch_dequant(const dqk_cache &c, float *k_out, float *v_out, hipStr
 hipError_t launch_bf16_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                               const int32_t *lengths, int batch, int hq, int hkv, int d, int ld_t,
                               float sm_scale, int split, float *out, float *ws, hipStream_t s);
+hipError_t launch_combine(const float *ws, int batch, int hq, int hkv, int d, int nsplit,
+                          float *out, hipStream_t s);
 hipError_t launch_f16_convert(const float *x, uint16_t *out, size_t n, hipStream_t s);
 
-// Workspace: per work item (unit, split) and query head of its group: m, l, o[d].
-inline size_t partial_floats(int d) { return (size_t)d + 2; }
+// Workspace: per work item (unit, split) and query head of its group:
+// m, l, two pad floats (keeps o 16-byte aligned), o[d].
+constexpr int kPartialHead = 4;
+inline size_t partial_floats(int d) { return (size_t)d + kPartialHead; }
 inline int num_splits(int cap_tokens, int split) { return (cap_tokens + split - 1) / split; }
 
 }  // namespace dqk

@@ -8,10 +8,11 @@
 // |q'|, equal magnitudes going to the lower index; the kept set is written in
 // ascending order.
 //
-// One workgroup per (batch row, query head), one wavefront-pair of 128 lanes:
-// lane j forms q'_j as an fp32 FMA chain over input channels in ascending order
-// (bit-reproducible), then ranks |q'_j| against the other channels -- an exact
-// top-k by counting -- and a ballot prefix gives each kept channel its slot.
+// One workgroup of 128 lanes per (batch row, KV head) serves the group's query
+// heads: lane j forms q'_j of every head as an fp32 FMA chain over input
+// channels in ascending order (bit-reproducible); then one wavefront per head
+// finds the exact top-k by a bitwise search over the magnitudes' bit patterns
+// with ballots, and ballot prefixes give each kept channel its ascending slot.
 // Built with -ffp-contract=off.
 #include "dqk_internal.h"
 
@@ -19,61 +20,106 @@ namespace dqk {
 namespace {
 
 constexpr int kThreads = 128;
+constexpr int kBatchRows = 16;   // rows of A loaded per batch (independent loads in flight)
 
+__device__ __forceinline__ int popc(unsigned long long m) { return __popcll(m); }
+
+// Exact top-(k) of one head's |q'| over channels 1..D-1 inside one wavefront:
+// lane l holds channels l and l+64.  Magnitudes are non-negative floats, so
+// their bit patterns order like the values; a 31-step bitwise search finds the
+// k-th largest pattern T, channels above T are kept, and of the channels equal
+// to T the lowest indices are kept.  Writes idx[0..keep) ascending.
 template <int D>
+__device__ void select_one_head(const float *mag, int keep, int32_t *idx) {
+  const int lane = threadIdx.x & 63;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  const int c0 = lane, c1 = lane + 64;
+  const bool v0 = c0 >= 1 && c0 < D, v1 = c1 < D;
+  const uint32_t k0 = v0 ? __float_as_uint(mag[c0]) : 0u;
+  const uint32_t k1 = v1 ? __float_as_uint(mag[c1]) : 0u;
+  const int want = keep - 1;             // channels to keep besides channel 0
+  bool s0 = false, s1 = false;
+  if (want > 0) {
+    uint32_t t = 0;
+    for (int bit = 30; bit >= 0; --bit) {
+      const uint32_t cand = t | (1u << bit);
+      const int n = popc(__ballot(v0 && k0 >= cand)) + popc(__ballot(v1 && k1 >= cand));
+      if (n >= want) t = cand;
+    }
+    const unsigned long long g0 = __ballot(v0 && k0 > t), g1 = __ballot(v1 && k1 > t);
+    const unsigned long long e0 = __ballot(v0 && k0 == t), e1 = __ballot(v1 && k1 == t);
+    const int need = want - popc(g0) - popc(g1);   // equal channels still to take
+    const int r0 = popc(e0 & below), r1 = popc(e0) + popc(e1 & below);
+    s0 = (v0 && k0 > t) || (v0 && k0 == t && r0 < need);
+    s1 = (v1 && k1 > t) || (v1 && k1 == t && r1 < need);
+  }
+  if (c0 == 0) s0 = true;                // the protected channel
+  const unsigned long long m0 = __ballot(s0), m1 = __ballot(s1);
+  if (s0) idx[popc(m0 & below)] = c0;
+  if (s1) idx[popc(m0) + popc(m1 & below)] = c1;
+}
+
+// One workgroup per (batch row, KV head); the G query heads of the group share
+// every load of A_g.  Lane j forms q'_j of all G heads; each wavefront then
+// selects for every other head.
+template <int D, int G>
 __global__ __launch_bounds__(kThreads) void select_kernel(const void *q, int bf16,
                                                           const float *__restrict__ amat, int hq,
                                                           int hkv, int keep, float *q_prime,
                                                           int32_t *sel_idx) {
-  __shared__ float qs[D];
-  __shared__ float mag[D];
-  __shared__ int kept[D];
-  const int row = blockIdx.x;  // b * hq + h
-  const int h = row % hq;
-  const int g = h / (hq / hkv);
-  const int j = threadIdx.x;
-  if (j < D)
-    qs[j] = bf16 ? bf16_value(static_cast<const uint16_t *>(q)[(size_t)row * D + j])
-                 : static_cast<const float *>(q)[(size_t)row * D + j];
+  __shared__ float qs[G][D];
+  __shared__ float mag[G][D];
+  const int b = blockIdx.x / hkv, g = blockIdx.x % hkv;
+  const size_t row0 = (size_t)b * hq + (size_t)g * G;
+  const int j = threadIdx.x, wave = j >> 6;
+  for (int e = j; e < G * D; e += kThreads)
+    qs[e / D][e % D] = bf16 ? bf16_value(static_cast<const uint16_t *>(q)[row0 * D + e])
+                            : static_cast<const float *>(q)[row0 * D + e];
   __syncthreads();
   if (j < D) {
+    float acc[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) acc[h] = 0.0f;
     const float *acol = amat + (size_t)g * D * D + j;
-    float acc = 0.0f;
-    for (int i = 0; i < D; ++i) acc = __builtin_fmaf(qs[i], acol[(size_t)i * D], acc);
-    q_prime[(size_t)row * D + j] = acc;
-    mag[j] = fabsf(acc);
-  }
-  __syncthreads();
-  if (j < D) {
-    int k = 1;  // channel 0 is always kept
-    if (j > 0) {
-      const float mj = mag[j];
-      int rank = 0;
-      for (int c = 1; c < D; ++c) rank += (mag[c] > mj) || (mag[c] == mj && c < j);
-      k = rank < keep - 1;
+    for (int i0 = 0; i0 < D; i0 += kBatchRows) {
+      float a[kBatchRows];
+#pragma unroll
+      for (int r = 0; r < kBatchRows; ++r) a[r] = acol[(size_t)(i0 + r) * D];
+#pragma unroll
+      for (int r = 0; r < kBatchRows; ++r)
+#pragma unroll
+        for (int h = 0; h < G; ++h) acc[h] = __builtin_fmaf(qs[h][i0 + r], a[r], acc[h]);
     }
-    kept[j] = k;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      q_prime[(row0 + h) * D + j] = acc[h];
+      mag[h][j] = fabsf(acc[h]);
+    }
   }
   __syncthreads();
-  if (j < D && kept[j]) {
-    int pos = 0;
-    for (int c = 0; c < j; ++c) pos += kept[c];
-    if (pos < keep) sel_idx[(size_t)row * keep + pos] = j;
+  for (int h = wave; h < G; h += kThreads / 64) select_one_head<D>(mag[h], keep, sel_idx + (row0 + h) * keep);
+}
+
+template <int D>
+hipError_t launch_d(const void *q, bool bf16, const float *amat, int batch, int hq, int hkv,
+                    int keep, float *q_prime, int32_t *sel_idx, hipStream_t s) {
+  const dim3 grid((unsigned)(batch * hkv));
+  switch (hq / hkv) {
+    case 1: hipLaunchKernelGGL((select_kernel<D, 1>), grid, dim3(kThreads), 0, s, q, (int)bf16, amat, hq, hkv, keep, q_prime, sel_idx); break;
+    case 2: hipLaunchKernelGGL((select_kernel<D, 2>), grid, dim3(kThreads), 0, s, q, (int)bf16, amat, hq, hkv, keep, q_prime, sel_idx); break;
+    case 4: hipLaunchKernelGGL((select_kernel<D, 4>), grid, dim3(kThreads), 0, s, q, (int)bf16, amat, hq, hkv, keep, q_prime, sel_idx); break;
+    case 8: hipLaunchKernelGGL((select_kernel<D, 8>), grid, dim3(kThreads), 0, s, q, (int)bf16, amat, hq, hkv, keep, q_prime, sel_idx); break;
+    default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_select(const void *q, bool bf16, const float *amat, int batch, int hq, int hkv,
                          int d, int keep, float *q_prime, int32_t *sel_idx, hipStream_t s) {
-  const dim3 grid((unsigned)(batch * hq));
-  if (d == 64)
-    hipLaunchKernelGGL(select_kernel<64>, grid, dim3(kThreads), 0, s, q, (int)bf16, amat, hq, hkv,
-                       keep, q_prime, sel_idx);
-  else
-    hipLaunchKernelGGL(select_kernel<128>, grid, dim3(kThreads), 0, s, q, (int)bf16, amat, hq,
-                       hkv, keep, q_prime, sel_idx);
-  return hipGetLastError();
+  if (d == 64) return launch_d<64>(q, bf16, amat, batch, hq, hkv, keep, q_prime, sel_idx, s);
+  return launch_d<128>(q, bf16, amat, batch, hq, hkv, keep, q_prime, sel_idx, s);
 }
 
 }  // namespace dqk

@@ -105,7 +105,7 @@ dqk_status dqk_transform_quantize_append(const dqk_cache *cache, const void *k_n
  * ascending order, channel 0 plus the keep-1 channels c >= 1 of largest |q'_c|,
  * equal magnitudes going to the lower index.
  * q: [batch][hq][d] of `dtype`; amat: [hkv][d][d] fp32; q_prime: [batch][hq][d]
- * fp32; sel_idx: [batch][hq][keep] i32; 1 <= keep <= d. */
+ * fp32; sel_idx: [batch][hq][keep] i32; 1 <= keep <= d; hq/hkv in {1, 2, 4, 8}. */
 dqk_status dqk_select_channels(const void *q, dqk_dtype dtype, const float *amat,
                                int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim,
                                int32_t keep, float *q_prime, int32_t *sel_idx,
@@ -122,8 +122,9 @@ dqk_status dqk_decode_workspace_bytes(const dqk_cache *cache, int32_t hq,
  *   out[b][h] = sum_t softmax(z)_t v~_t        (T = 0 gives zeros)
  * where k~ is channel 0's fp16 value, the 2-bit value of complete groups, or the
  * exact tail.  Only the kept key channels' codes and scales are read from HBM.
- * The sequence is split into chunks of split_tokens (a multiple of 32; 0 = the
- * library's choice) reduced with an online-max combine.  fp32 accumulation.
+ * The sequence is split into chunks of split_tokens (a multiple of 32 and at
+ * most 8192/(hq/hkv); 0 = the library's choice) reduced with an online-max
+ * combine.  Products run on the matrix cores with fp32 accumulation.
  * q_prime: [batch][hq][d] fp32; sel_idx: [batch][hq][keep] as produced by
  * dqk_select_channels; out: [batch][hq][d] fp32; workspace: device scratch of at
  * least dqk_decode_workspace_bytes (contents need no initialization). */

@@ -63,15 +63,18 @@ def test_cache_validation_without_gpu():
     L = M.lib()
     out = C.c_size_t(0)
     assert L.dqk_decode_workspace_bytes(C.byref(fake_cache()), 8, 0, C.byref(out)) == OK
-    assert out.value == 2 * 2 * 1 * 4 * 130 * 4          # 1 split of 1024 covers 256 tokens
+    assert out.value == 2 * 2 * 1 * 4 * 132 * 4          # 1 default split covers 256 tokens
     assert L.dqk_decode_workspace_bytes(C.byref(fake_cache()), 8, 64, C.byref(out)) == OK
-    assert out.value == 2 * 2 * 4 * 4 * 130 * 4
+    assert out.value == 2 * 2 * 4 * 4 * 132 * 4
     for bad in (dict(capacity=100), dict(batch=0), dict(k_codes=0), dict(v_codes=0x10004),
                 dict(lengths=0)):
         assert L.dqk_decode_workspace_bytes(C.byref(fake_cache(**bad)), 8, 0, C.byref(out)) == INVALID
     assert L.dqk_decode_workspace_bytes(C.byref(fake_cache(head_dim=96)), 8, 0, C.byref(out)) == UNSUPPORTED
     assert L.dqk_decode_workspace_bytes(C.byref(fake_cache()), 6, 0, C.byref(out)) == UNSUPPORTED
     assert L.dqk_decode_workspace_bytes(C.byref(fake_cache()), 8, 48, C.byref(out)) == INVALID
+    assert L.dqk_decode_workspace_bytes(C.byref(fake_cache()), 8, 2048, C.byref(out)) == OK
+    assert L.dqk_decode_workspace_bytes(C.byref(fake_cache()), 8, 2080, C.byref(out)) == INVALID
+    assert L.dqk_decode_workspace_bytes(C.byref(fake_cache()), 16, 1056, C.byref(out)) == INVALID
     assert L.dqk_decode_workspace_bytes(None, 8, 0, C.byref(out)) == INVALID
 
 
@@ -118,7 +121,7 @@ def test_bf16_decode_validation_without_gpu():
     L = M.lib()
     out = C.c_size_t(0)
     assert L.dqk_bf16_decode_workspace_bytes(1, 32, 8, 128, 131072, 0, C.byref(out)) == OK
-    assert out.value == 8 * 128 * 4 * 130 * 4
+    assert out.value == 8 * 128 * 4 * 132 * 4
     assert L.dqk_bf16_decode_workspace_bytes(1, 32, 8, 96, 1024, 0, C.byref(out)) == UNSUPPORTED
     args = [0x20000, 0x30000, 0x40000, 0x50000, 1, 32, 8, 128, 1024, 0.1, 0, 0x60000, 0x70000,
             1 << 30, None]

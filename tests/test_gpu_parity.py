@@ -180,7 +180,7 @@ def test_decode_tiny_full(orc):
 
 def test_decode_gqa_reduced(orc):
     wl = W.workload("gqa8k", batch=2, ctx=2500)
-    decode_case(orc, wl, splits=(0, 64, 1024, 4096))
+    decode_case(orc, wl, splits=(0, 64, 1024, 2048))
     decode_case(orc, wl, sm_mult=0.01, splits=(0, 352))
     decode_case(orc, wl, sparsity=0)
     decode_case(orc, wl, sparsity=60, sm_mult=0.02)
