@@ -71,42 +71,92 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+// Cross-lane reductions with DPP moves (no LDS traffic).  `idn` fills lanes the
+// move does not write, so it must be the identity of the operation.
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ float dpp_mov(float idn, float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, idn),
+                                                              __builtin_bit_cast(int, v), CTRL,
+                                                              ROWS, 0xf, false));
+}
+__device__ __forceinline__ float row16_max(float x) {   // every lane: max over its 16-lane row
+  x = fmaxf(x, dpp_mov<0xB1>(x, x));   // quad_perm [1,0,3,2]  (max is idempotent: fill = x)
+  x = fmaxf(x, dpp_mov<0x4E>(x, x));   // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp_mov<0x141>(x, x));  // row_half_mirror
+  x = fmaxf(x, dpp_mov<0x140>(x, x));  // row_mirror
   return x;
 }
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+__device__ __forceinline__ float row16_sum(float x) {   // every lane: sum over its 16-lane row
+  x += dpp_mov<0xB1>(0.0f, x);
+  x += dpp_mov<0x4E>(0.0f, x);
+  x += dpp_mov<0x141>(0.0f, x);
+  x += dpp_mov<0x140>(0.0f, x);
   return x;
 }
-__device__ __forceinline__ float row16_sum(float x) {  // sum over the 16 lanes of a row
-#pragma unroll
-  for (int o = 8; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
-  return x;
+__device__ __forceinline__ float wave_max(float x) {    // uniform result
+  x = row16_max(x);
+  x = fmaxf(x, dpp_mov<0x142, 0xa>(x, x));  // row_bcast:15
+  x = fmaxf(x, dpp_mov<0x143, 0xc>(x, x));  // row_bcast:31
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
 }
+__device__ __forceinline__ float wave_sum(float x) {    // uniform result
+  x = row16_sum(x);
+  x += dpp_mov<0x142, 0xa>(0.0f, x);
+  x += dpp_mov<0x143, 0xc>(0.0f, x);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+
+// Keeps a constant in a VGPR so (x & m) | c selects one v_and_or_b32 (gfx9 VOP3
+// takes no literals and at most one scalar operand).
+__device__ __forceinline__ uint32_t in_vgpr(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+constexpr int kTok = 64;   // tokens per wavefront tile (two key groups)
+constexpr int kYRow = kTok / 4 * 2 + 8;   // dwords per channel octet in the key staging, padded
+
+
+template <int D, int G>
+struct Cfg {
+  static constexpr int VG = D / kGroup;        // value scale groups per token
+  static constexpr int KCM = D / 32;           // key K-chunks of 32 union slots (max)
+  static constexpr int OCT = D / 8;            // channel octets
+  static constexpr int NTT = D / 16;           // value N-tiles of 16 channels
+  static constexpr int KQ = D / 8;             // union-slot octets per head
+  static constexpr int AREP = (KQ * G + 63) / 64;
+  static constexpr int NGB = G <= 4 ? 2 : 1;   // key groups whose A operands are built together
+  static constexpr int HS = (G + 3) / 4;       // head sets of the compact numerator build
+  static constexpr int VWR = D / 64;           // 16-byte value chunks per lane per tile
+  static constexpr int KEY_A = NGB * KCM * 4 * (2 * G) * 4;   // rows 2h (high), 2h+1 (low)
+  static constexpr int VAL_A = 2 * VG * 4 * G * 4;
+  static constexpr int ABUF = KEY_A > VAL_A ? KEY_A : VAL_A;   // dwords
+};
+
+template <int D, int G>
+struct WaveSmem {
+  union {
+    struct {
+      uint32_t y[D / 8][kYRow];        // key codes: channel octet, (token quad, 4 ch + 4 ch), padded
+      float ksig[2][D];                // key scales of the tile's two groups, U order
+      float ch0[kTok];                 // channel-0 keys
+      uint32_t vw[kTok / 16][D + 16];  // value code words (rows padded against bank conflicts)
+      float vsig[D / kGroup][kTok];    // value scales, by value group
+    } st;
+    float merge[G][D];                 // this wavefront's output at the end of the split
+  } u;
+  float z[G][kTok + 1];                // logits, then numerators, of the tile (padded rows)
+  uint32_t abuf[Cfg<D, G>::ABUF];      // MFMA A operands (compact build, MFMA-layout reads)
+  float mstate[G], lstate[G];
+};
 
 template <int D, int G>
 struct Smem {
-  union {
-    struct {
-      uint32_t y[D / 8][kTile / 4][2];  // key codes: channel octet, token quad, (4 ch, 4 ch)
-      float sig[kTileGroups][D];        // key scales of the tile's groups, U order
-      float ch0[kTile];                 // channel-0 keys of the tile
-    } k;
-    struct {
-      uint32_t w[kTile / 16][D];        // value code words of the tile
-      float sig[kTile][D / kGroup];     // value scales * 2^F
-    } v;
-  } st;
-  uint32_t a[kWaves][D / 32][64][4];    // per-wavefront MFMA A operands
-  float z[G][kMaxSplitTokensTimesG / G];  // logits of the split, then numerators
-  float coefc[G][D];                    // q' * sm * log2(e) by channel (0 if dropped)
-  float coefs[G][D];                    // coefc in U order * 2^-E_h (0 past |U|)
-  float e8[G];                          // 8 * 2^E_h
-  float redm[G][kWaves], redl[G][kWaves];
-  float redf[kWaves];
+  WaveSmem<D, G> w[kWaves];
+  float coefc[G][D];                   // q' * sm * log2(e) by channel (0 if dropped)
+  float coefs[G][D];                   // coefc in U order * 2^-E_h (0 past |U|)
+  float e8[G];                         // 8 * 2^E_h
+  float redm[G][kWaves];
   int hmask[D];
   int16_t ulist[D];
   int wcount[2];
@@ -119,14 +169,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(dqk_cache c,
                                                              int hq, int keep, float scale2,
                                                              int split, int nsplit,
                                                              float *__restrict__ ws) {
+  using K = Cfg<D, G>;
   __shared__ Smem<D, G> sm;
-  constexpr int VG = D / kGroup;      // value scale groups per token
-  constexpr int KCM = D / 32;         // K-chunks of 32 union slots (max)
-  constexpr int OCT = D / 8;          // channel octets
-  constexpr int NTW = D / 64;         // value N-tiles (16 channels) per wavefront
-  constexpr int KQ = D / 8;           // union-slot octets per head
-  constexpr int AREP = (KQ * G + 63) / 64;    // compact key A items per lane
-  constexpr int AREPV = (16 * G + 63) / 64;   // compact value A items per lane
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n16 = lane & 15, kg = lane >> 4;
   const int item = blockIdx.x;
@@ -149,17 +193,13 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(dqk_cache c,
   const uint16_t *c0row = c.k_ch0 + unit * (size_t)c.capacity;
   const float *tail = c.k_tail + unit * (size_t)kGroup * D;
   const uint32_t *vwords = c.v_codes + unit * (size_t)(c.capacity / 16) * D;
-  const uint16_t *vscales = c.v_scales + unit * (size_t)c.capacity * VG;
+  const uint16_t *vscales = c.v_scales + unit * (size_t)c.capacity * K::VG;
   const int t_body = (len / kGroup) * kGroup;
   const int code_end = min(t_body, t_end);
 
-  // ---------------------------------------------------------------- setup
+  // ---------------------------------------------------------------- setup (whole workgroup)
   for (int e = tid; e < G * D; e += kThreads) sm.coefc[e / D][e % D] = 0.0f;
   for (int e = tid; e < D; e += kThreads) sm.hmask[e] = 0;
-  {
-    uint32_t *a = &sm.a[0][0][0][0];
-    for (int e = tid; e < kWaves * KCM * 64 * 4; e += kThreads) a[e] = 0u;
-  }
   __syncthreads();
   const size_t row0 = (size_t)b * hq + (size_t)g * G;
   for (int e = tid; e < G * keep; e += kThreads) {
@@ -175,9 +215,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(dqk_cache c,
     const bool f = tid < D && tid >= 1 && sm.hmask[tid] != 0;
     const unsigned long long m = __ballot(f);
     if (lane == 0 && wave < 2) sm.wcount[wave] = __popcll(m);
-    // largest |coefficient| of each head over channels >= 1
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
+    for (int h = 0; h < G; ++h) {   // largest |coefficient| of each head over channels >= 1
       const float v = (tid >= 1 && tid < D) ? fabsf(sm.coefc[h][tid]) : 0.0f;
       const float mx = wave_max(v);
       if (lane == 0) sm.redm[h][wave] = mx;
@@ -185,14 +224,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(dqk_cache c,
     __syncthreads();
     if (f) sm.ulist[__popcll(m & ((1ull << lane) - 1ull)) + (wave == 1 ? sm.wcount[0] : 0)] = (int16_t)tid;
   }
-  // scale exponent of the value pass: 2^F * max value scale of the split < 2^15
-  float vmax = 0.0f;
-  for (int t = t_begin + tid; t < t_end; t += kThreads) {
-#pragma unroll
-    for (int j = 0; j < VG; ++j) vmax = fmaxf(vmax, f16_value(vscales[(size_t)t * VG + j]));
-  }
-  vmax = wave_max(vmax);
-  if (lane == 0) sm.redf[wave] = vmax;
   __syncthreads();
   const int nu = sm.wcount[0] + sm.wcount[1];
   const int nkc = (nu + 31) / 32;
@@ -206,301 +237,395 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(dqk_cache c,
     sm.coefs[h][i] = i < nu ? sm.coefc[h][sm.ulist[i]] * ldexpf(1.0f, -ex) : 0.0f;
     if (i == 0) sm.e8[h] = ldexpf(8.0f, ex);
   }
-  float fscale;
-  {
-    float vm = sm.redf[0];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) vm = fmaxf(vm, sm.redf[w]);
-    int ev = 0;
-    if (vm > 0.0f) frexpf(vm, &ev);
-    fscale = ldexpf(1.0f, 15 - ev);
-  }
   __syncthreads();
 
-  // my fixed share of the compact A build: (head, 8 consecutive union slots)
-  float myc[AREP][8];
+  // ---------------------------------------------------------------- per-wavefront state
+  WaveSmem<D, G> &W = sm.w[wave];
+  float myc[K::AREP][8];   // my share of the key A build: (head, 8 union slots)
 #pragma unroll
-  for (int rep = 0; rep < AREP; ++rep) {
+  for (int rep = 0; rep < K::AREP; ++rep) {
     const int it = lane + 64 * rep;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) myc[rep][i] = it < KQ * G ? sm.coefs[it / KQ][8 * (it % KQ) + i] : 0.0f;
+    for (int i = 0; i < 8; ++i) myc[rep][i] = it < K::KQ * G ? sm.coefs[it / K::KQ][8 * (it % K::KQ) + i] : 0.0f;
   }
+  // my staging share: key code rows of channel octet lane/4, scale rows of channels lane, lane+64
+  const int so = lane >> 2, swb = lane & 3;
 
-  // ---------------------------------------------------------------- key pass
-  for (int tile0 = t_begin; tile0 < t_end; tile0 += kTile) {
-    {  // stage key codes, re-interleaved: thread = (octet, 16-token block)
-      const int o = tid >> 4, wb = tid & 15;
-      const int tok = tile0 + 16 * wb;
-      if (o < OCT) {
-        uint32_t x[8];
+  const int nv = t_end - t_begin;
+  const int ntiles = (nv + kTok - 1) / kTok;
+
+  // prefetch registers
+  uint32_t px[8];
+  uint16_t pks[2][2];
+  uint16_t pc0;
+  u32x4 pvw[K::VWR];
+  uint16_t pvs[K::VG];
+
+  // Loads of the next tile: addresses are clamped to the unit's first element when
+  // the data is absent, and the value is replaced by zero (no branches).
+  auto issue = [&](int tk) {
+    const int p0 = t_begin + kTok * tk;
+    const int tok = p0 + 16 * swb;
+    const bool tok_ok = tok < code_end;
 #pragma unroll
-        for (int cc = 0; cc < 8; ++cc) {
-          const int i = 8 * o + cc;
-          x[cc] = (i < nu && tok < code_end)
-                      ? *reinterpret_cast<const uint32_t *>(kcodes + (size_t)sm.ulist[i] * kc_stride + (tok >> 2))
-                      : 0u;
-        }
-        uint32_t y0[4], y1[4];
-        {
-          const uint32_t a = __builtin_amdgcn_perm(x[0], x[2], 0x05010400u);
-          const uint32_t bb = __builtin_amdgcn_perm(x[1], x[3], 0x05010400u);
-          const uint32_t a2 = __builtin_amdgcn_perm(x[0], x[2], 0x07030602u);
-          const uint32_t b2 = __builtin_amdgcn_perm(x[1], x[3], 0x07030602u);
-          y0[0] = __builtin_amdgcn_perm(bb, a, 0x05040100u);
-          y0[1] = __builtin_amdgcn_perm(bb, a, 0x07060302u);
-          y0[2] = __builtin_amdgcn_perm(b2, a2, 0x05040100u);
-          y0[3] = __builtin_amdgcn_perm(b2, a2, 0x07060302u);
-        }
-        {
-          const uint32_t a = __builtin_amdgcn_perm(x[4], x[6], 0x05010400u);
-          const uint32_t bb = __builtin_amdgcn_perm(x[5], x[7], 0x05010400u);
-          const uint32_t a2 = __builtin_amdgcn_perm(x[4], x[6], 0x07030602u);
-          const uint32_t b2 = __builtin_amdgcn_perm(x[5], x[7], 0x07030602u);
-          y1[0] = __builtin_amdgcn_perm(bb, a, 0x05040100u);
-          y1[1] = __builtin_amdgcn_perm(bb, a, 0x07060302u);
-          y1[2] = __builtin_amdgcn_perm(b2, a2, 0x05040100u);
-          y1[3] = __builtin_amdgcn_perm(b2, a2, 0x07060302u);
-        }
-        u32x4 *dst = reinterpret_cast<u32x4 *>(&sm.st.k.y[o][4 * wb][0]);
-        dst[0] = u32x4{y0[0], y1[0], y0[1], y1[1]};
-        dst[1] = u32x4{y0[2], y1[2], y0[3], y1[3]};
-      }
+    for (int cc = 0; cc < 8; ++cc) {
+      const int i = 8 * so + cc;
+      const bool ok = so < K::OCT && i < nu && tok_ok;
+      const size_t off = ok ? (size_t)sm.ulist[i] * kc_stride + (tok >> 2) : 0;
+      const uint32_t x = *reinterpret_cast<const uint32_t *>(kcodes + off);
+      px[cc] = ok ? x : 0u;
     }
-    if (tid < D) {  // key scales of the tile's groups (zero past the coded tokens)
 #pragma unroll
-      for (int gg = 0; gg < kTileGroups; ++gg) {
-        const int grp = tile0 / kGroup + gg;
-        sm.st.k.sig[gg][tid] = (tid < nu && grp * kGroup < code_end)
-                                   ? f16_value(kscales[(size_t)sm.ulist[tid] * ks_stride + grp])
-                                   : 0.0f;
+    for (int cc = 0; cc < 2; ++cc) {
+      const int i = lane + 64 * cc;
+      const bool ok = i < nu;
+      const size_t row = ok ? (size_t)sm.ulist[i] * ks_stride : 0;
+#pragma unroll
+      for (int gq = 0; gq < 2; ++gq) {
+        const int grp = p0 / kGroup + gq;
+        const bool okg = ok && grp * kGroup < code_end;
+        const uint16_t x = kscales[okg ? row + grp : 0];
+        pks[cc][gq] = okg ? x : (uint16_t)0;
       }
     }
     {
-      const int t = tile0 + tid;
-      sm.st.k.ch0[tid] = t < t_end ? f16_value(c0row[t]) : 0.0f;
+      const bool ok = p0 + lane < t_end;
+      const uint16_t x = c0row[ok ? p0 + lane : 0];
+      pc0 = ok ? x : (uint16_t)0;
     }
-    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < K::VWR; ++r) {
+      const int e = lane + 64 * r;
+      const int blk = e / (D / 4), c4 = e % (D / 4);
+      const int tokb = p0 + 16 * blk;
+      const bool ok = tokb < t_end;
+      const u32x4 x = *reinterpret_cast<const u32x4 *>(vwords + (ok ? (size_t)(tokb >> 4) * D + 4 * c4 : 0));
+      pvw[r] = ok ? x : u32x4{0u, 0u, 0u, 0u};
+    }
+    {
+      const bool ok = p0 + lane < t_end;
+      const size_t base = ok ? (size_t)(p0 + lane) * K::VG : 0;
+#pragma unroll
+      for (int j = 0; j < K::VG; ++j) {
+        const uint16_t x = vscales[base + j];
+        pvs[j] = ok ? x : (uint16_t)0;
+      }
+    }
+  };
 
-    // wavefront w: key groups 2w and 2w+1 of the tile
-#pragma unroll 1
-    for (int gq = 0; gq < 2; ++gq) {
-      const int gg = 2 * wave + gq;
-      if (tile0 + kGroup * gg >= t_end) break;  // wavefront-uniform
-      // compact A build: (head h, union slots 8kq..8kq+7) -> rows h (high) and G+h (low)
-#pragma unroll
-      for (int rep = 0; rep < AREP; ++rep) {
-        const int it = lane + 64 * rep;
-        if (it < KQ * G) {
-          const int h = it / KQ, kq = it % KQ;
-          const float *sg = &sm.st.k.sig[gg][8 * kq];
-          uint32_t hi[4], lo[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float a0 = myc[rep][2 * i] * sg[2 * i];
-            const float a1 = myc[rep][2 * i + 1] * sg[2 * i + 1];
-            hi[i] = f16_pair(a0, a1);
-            lo[i] = f16_pair(a0 - f16_low(hi[i]), a1 - f16_high(hi[i]));
-          }
-          const int kcx = kq >> 2, kgx = kq & 3;
-          *reinterpret_cast<u32x4 *>(&sm.a[wave][kcx][16 * kgx + h][0]) = u32x4{hi[0], hi[1], hi[2], hi[3]};
-          *reinterpret_cast<u32x4 *>(&sm.a[wave][kcx][16 * kgx + G + h][0]) = u32x4{lo[0], lo[1], lo[2], lo[3]};
-        }
+  auto commit = [&]() {
+    if (so < K::OCT) {
+      uint32_t y0[4], y1[4];
+      {
+        const uint32_t a = __builtin_amdgcn_perm(px[0], px[2], 0x05010400u);
+        const uint32_t bb = __builtin_amdgcn_perm(px[1], px[3], 0x05010400u);
+        const uint32_t a2 = __builtin_amdgcn_perm(px[0], px[2], 0x07030602u);
+        const uint32_t b2 = __builtin_amdgcn_perm(px[1], px[3], 0x07030602u);
+        y0[0] = __builtin_amdgcn_perm(bb, a, 0x05040100u);
+        y0[1] = __builtin_amdgcn_perm(bb, a, 0x07060302u);
+        y0[2] = __builtin_amdgcn_perm(b2, a2, 0x05040100u);
+        y0[3] = __builtin_amdgcn_perm(b2, a2, 0x07060302u);
       }
-      wave_sync();
-      f32x4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = acc0, accs = acc0;
-      const int r2 = 2 * (n16 & 3);
-      const u32x4 ones = {kOne2, kOne2, kOne2, kOne2};
-      for (int kc = 0; kc < nkc; ++kc) {
-        const u32x4 A = *reinterpret_cast<const u32x4 *>(&sm.a[wave][kc][lane][0]);
-        const int oct = 4 * kc + kg;
-        const uint32_t *y = &sm.st.k.y[oct][8 * gg + (n16 >> 2)][0];
-        const uint32_t y00 = y[0], y01 = y[1];           // N-tile 0 (tokens 0..15 of the group)
-        const uint32_t y10 = y[8], y11 = y[9];           // N-tile 1 (quad + 4)
-        const u32x4 b0 = {((y00 >> r2) & kCode2) | kOne2, ((y00 << (8 - r2)) & kCode2) | kOne2,
-                          ((y01 >> r2) & kCode2) | kOne2, ((y01 << (8 - r2)) & kCode2) | kOne2};
-        const u32x4 b1 = {((y10 >> r2) & kCode2) | kOne2, ((y10 << (8 - r2)) & kCode2) | kOne2,
-                          ((y11 >> r2) & kCode2) | kOne2, ((y11 << (8 - r2)) & kCode2) | kOne2};
-        acc0 = mfma16(A, b0, acc0);
-        acc1 = mfma16(A, b1, acc1);
-        accs = mfma16(A, ones, accs);
+      {
+        const uint32_t a = __builtin_amdgcn_perm(px[4], px[6], 0x05010400u);
+        const uint32_t bb = __builtin_amdgcn_perm(px[5], px[7], 0x05010400u);
+        const uint32_t a2 = __builtin_amdgcn_perm(px[4], px[6], 0x07030602u);
+        const uint32_t b2 = __builtin_amdgcn_perm(px[5], px[7], 0x07030602u);
+        y1[0] = __builtin_amdgcn_perm(bb, a, 0x05040100u);
+        y1[1] = __builtin_amdgcn_perm(bb, a, 0x07060302u);
+        y1[2] = __builtin_amdgcn_perm(b2, a2, 0x05040100u);
+        y1[3] = __builtin_amdgcn_perm(b2, a2, 0x07060302u);
       }
-      wave_sync();
-      // rows r = 4*kg + i; high part row h, low part row G+h
+      u32x4 *dst = reinterpret_cast<u32x4 *>(&W.u.st.y[so][8 * swb]);
+      dst[0] = u32x4{y0[0], y1[0], y0[1], y1[1]};
+      dst[1] = u32x4{y0[2], y1[2], y0[3], y1[3]};
+    }
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const f32x4 acc = nt == 0 ? acc0 : acc1;
-        float v[4];
+    for (int cc = 0; cc < 2; ++cc) {
+      const int i = lane + 64 * cc;
+      if (i < D) {
+        W.u.st.ksig[0][i] = f16_value(pks[cc][0]);
+        W.u.st.ksig[1][i] = f16_value(pks[cc][1]);
+      }
+    }
+    W.u.st.ch0[lane] = f16_value(pc0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = acc[i] - 1.375f * accs[i];
-        const int tokl = kGroup * gg + 16 * nt + n16;   // token within the tile
-        const int t = tile0 + tokl;
-        const float x0 = sm.st.k.ch0[tokl];
-        if (G >= 4) {
-          constexpr int OFF = 4 * G;  // lanes between high and low rows
-          float w[4];
+    for (int r = 0; r < K::VWR; ++r) {
+      const int e = lane + 64 * r;
+      const int blk = e / (D / 4), c4 = e % (D / 4);
+      *reinterpret_cast<u32x4 *>(&W.u.st.vw[blk][4 * c4]) = pvw[r];
+    }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) w[i] = v[i] + __shfl_xor(v[i], OFF, 64);
-          if (kg < G / 4) {
+    for (int j = 0; j < K::VG; ++j) W.u.st.vsig[j][lane] = f16_value(pvs[j]);
+  };
+
+  float m_run[G], l_run[G];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int h = 4 * kg + i;
-              const float zz = fmaf(sm.e8[h], w[i], sm.coefc[h][0] * x0);
-              sm.z[h][t - t_begin] = t < t_end ? zz : -INFINITY;
+  for (int h = 0; h < G; ++h) {
+    m_run[h] = -INFINITY;
+    l_run[h] = 0.0f;
+  }
+  bool f_set = false;
+  int f_run = 0;
+  f32x4 vacc[K::NTT];
+#pragma unroll
+  for (int nt = 0; nt < K::NTT; ++nt) vacc[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  float spart[K::HS][K::VG];   // sum of the fp16 numerators per (head, value group)
+#pragma unroll
+  for (int hs = 0; hs < K::HS; ++hs)
+#pragma unroll
+    for (int j = 0; j < K::VG; ++j) spart[hs][j] = 0.0f;
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  const u32x4 ones = {kOne2, kOne2, kOne2, kOne2};
+  const uint32_t vmask = in_vgpr(kCode2), vone = in_vgpr(kOne2);
+
+  if (wave < ntiles) {
+    issue(wave);
+    commit();
+  }
+  wave_sync();
+
+  for (int tk = wave; tk < ntiles; tk += kWaves) {
+    const int tile0 = t_begin + kTok * tk;
+    const bool more = tk + kWaves < ntiles;
+    if (more) issue(tk + kWaves);   // in flight during this tile's compute
+
+    // ---- logits of the tile's two key groups
+#pragma unroll
+    for (int gb = 0; gb < 2 / K::NGB; ++gb) {
+#pragma unroll
+      for (int q = 0; q < K::NGB; ++q) {
+        const int gq = gb * K::NGB + q;
+        if (tile0 + kGroup * gq < t_end) {
+#pragma unroll
+          for (int rep = 0; rep < K::AREP; ++rep) {
+            const int it = lane + 64 * rep;
+            if (it < K::KQ * G) {
+              const int h = it / K::KQ, kq = it % K::KQ;
+              const float *sg = &W.u.st.ksig[gq][8 * kq];
+              uint32_t hi[4], lo[4];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const float a0 = myc[rep][2 * i] * sg[2 * i];
+                const float a1 = myc[rep][2 * i + 1] * sg[2 * i + 1];
+                hi[i] = f16_pair(a0, a1);
+                lo[i] = f16_pair(a0 - f16_low(hi[i]), a1 - f16_high(hi[i]));
+              }
+              const int base = ((q * K::KCM + (kq >> 2)) * 4 + (kq & 3)) * (2 * G);
+              *reinterpret_cast<u32x4 *>(&W.abuf[4 * (base + 2 * h)]) = u32x4{hi[0], hi[1], hi[2], hi[3]};
+              *reinterpret_cast<u32x4 *>(&W.abuf[4 * (base + 2 * h + 1)]) = u32x4{lo[0], lo[1], lo[2], lo[3]};
             }
           }
-        } else if (kg == 0) {
+        }
+      }
+      wave_sync();
 #pragma unroll
-          for (int h = 0; h < G; ++h) {
-            const float zz = fmaf(sm.e8[h], v[h] + v[G + h], sm.coefc[h][0] * x0);
-            sm.z[h][t - t_begin] = t < t_end ? zz : -INFINITY;
+      for (int q = 0; q < K::NGB; ++q) {
+        const int gq = gb * K::NGB + q;
+        if (tile0 + kGroup * gq >= t_end) {   // wavefront-uniform: group past the split end
+          for (int e = lane; e < G * kGroup; e += 64) W.z[e / kGroup][kGroup * gq + e % kGroup] = -INFINITY;
+          continue;
+        }
+        f32x4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = acc0, accs = acc0;
+        const int r2 = 2 * (n16 & 3);
+        for (int kc = 0; kc < nkc; ++kc) {
+          const u32x4 A = n16 < 2 * G
+                              ? *reinterpret_cast<const u32x4 *>(&W.abuf[4 * (((q * K::KCM + kc) * 4 + kg) * (2 * G) + n16)])
+                              : zero4;
+          const uint32_t *y = &W.u.st.y[4 * kc + kg][2 * (8 * gq + (n16 >> 2))];
+          const uint32_t y00 = y[0], y01 = y[1], y10 = y[8], y11 = y[9];
+          const u32x4 b0 = {((y00 >> r2) & vmask) | vone, ((y00 << (8 - r2)) & vmask) | vone,
+                            ((y01 >> r2) & vmask) | vone, ((y01 << (8 - r2)) & vmask) | vone};
+          const u32x4 b1 = {((y10 >> r2) & vmask) | vone, ((y10 << (8 - r2)) & vmask) | vone,
+                            ((y11 >> r2) & vmask) | vone, ((y11 << (8 - r2)) & vmask) | vone};
+          acc0 = mfma16(A, b0, acc0);
+          acc1 = mfma16(A, b1, acc1);
+          accs = mfma16(A, ones, accs);
+        }
+        // C rows 4kg..4kg+3 = (high, low) of heads 2kg and 2kg+1: the sum stays in the lane
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          const f32x4 acc = nt == 0 ? acc0 : acc1;
+          const int tokl = kGroup * gq + 16 * nt + n16;   // token within the tile
+          const int t = tile0 + tokl;
+          const float x0 = W.u.st.ch0[tokl];
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const int h = 2 * kg + i;
+            if (h < G) {
+              const float v = (acc[2 * i] + acc[2 * i + 1]) - 1.375f * (accs[2 * i] + accs[2 * i + 1]);
+              const float zz = fmaf(sm.e8[h], v, sm.coefc[h][0] * x0);
+              W.z[h][tokl] = t < t_end ? zz : -INFINITY;
+            }
+          }
+        }
+      }
+      wave_sync();
+    }
+
+    // ---- tokens of the unfinished last group: exact fp32 tail keys
+    if (tile0 + kTok > t_body && t_body < t_end) {
+      const int ta = max(tile0, t_body), tb = min(tile0 + kTok, t_end);
+      const int nt = tb - ta;
+      for (int e = lane; e < G * nt; e += 64) {
+        const int h = e / nt, t = ta + e % nt;
+        float zz = sm.coefc[h][0] * f16_value(c0row[t]);
+        for (int i = 0; i < nu; ++i) {
+          const int ch = sm.ulist[i];
+          zz = fmaf(sm.coefc[h][ch], tail[(size_t)(t & 31) * D + ch], zz);
+        }
+        W.z[h][t - tile0] = zz;
+      }
+      wave_sync();
+    }
+
+    // ---- online softmax over the tile (lane = token)
+    float ra[4];            // factor of C row 4kg+i (head of that row)
+    float rs[K::HS];        // factor of head 4hs+kg (compact numerator sums)
+    bool moved = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ra[i] = 1.0f;
+#pragma unroll
+    for (int hs = 0; hs < K::HS; ++hs) rs[hs] = 1.0f;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float zv = W.z[h][lane];
+      const float m_new = fmaxf(m_run[h], wave_max(zv));
+      const float al = exp2f(m_run[h] - m_new);
+      const float p = exp2f(zv - m_new);
+      l_run[h] = fmaf(l_run[h], al, wave_sum(p));
+      m_run[h] = m_new;
+      W.z[h][lane] = p;
+      moved = moved || al != 1.0f;
+      if (h < 4) ra[h] = al;
+      else ra[h - 4] = (kg & 1) ? al : ra[h - 4];
+      rs[h >> 2] = ((h & 3) == kg) ? al : rs[h >> 2];
+    }
+    // value scale exponent: 2^f * (largest value scale seen) < 2^15
+    float vmx = 0.0f;
+#pragma unroll
+    for (int j = 0; j < K::VG; ++j) vmx = fmaxf(vmx, W.u.st.vsig[j][lane]);
+    vmx = wave_max(vmx);
+    int fe = 0;
+    if (vmx > 0.0f) frexpf(vmx, &fe);
+    const int f_tile = 15 - fe;
+    const int f_new = f_set ? min(f_run, f_tile) : f_tile;
+    const float factor = f_set ? ldexpf(1.0f, f_new - f_run) : 1.0f;
+    f_run = f_new;
+    f_set = true;
+    const float fs = ldexpf(1.0f, f_new);
+    // rescale the running sums only when a head's max or the exponent moved (uniform test)
+    if (moved || factor != 1.0f) {
+#pragma unroll
+      for (int nt = 0; nt < K::NTT; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vacc[nt][i] *= ra[i] * factor;
+#pragma unroll
+      for (int hs = 0; hs < K::HS; ++hs)
+#pragma unroll
+        for (int j = 0; j < K::VG; ++j) spart[hs][j] *= rs[hs] * factor;
+    }
+    wave_sync();
+
+    // ---- compact numerators p * s * 2^f -> A operands (row = head, K = token)
+#pragma unroll
+    for (int hs = 0; hs < K::HS; ++hs) {
+      const int h = 4 * hs + kg;
+      if (h < G) {
+        const int kgx = n16 >> 2, ii = n16 & 3;
+        const int r0 = 2 * (kgx & 1), d = ii & 1;
+        const int tl = 16 * (kgx >> 1) + (ii < 2 ? 4 + r0 + d : r0 + d);
+#pragma unroll
+        for (int kc2 = 0; kc2 < 2; ++kc2) {
+          const int t0 = 32 * kc2 + tl;
+          const float p0 = W.z[h][t0], p1 = W.z[h][t0 + 8];
+#pragma unroll
+          for (int j = 0; j < K::VG; ++j) {
+            const uint32_t pk = f16_pair(p0 * (W.u.st.vsig[j][t0] * fs), p1 * (W.u.st.vsig[j][t0 + 8] * fs));
+            spart[hs][j] += f16_low(pk) + f16_high(pk);
+            W.abuf[4 * ((((kc2 * K::VG + j) * 4 + kgx) * G) + h) + ii] = pk;
           }
         }
       }
     }
-    __syncthreads();
-  }
+    wave_sync();
 
-  // tokens of the unfinished last group: exact fp32 tail keys
-  {
-    const int ta = max(t_begin, t_body);
-    const int nt = t_end - ta;
-    for (int e = tid; e < G * max(nt, 0); e += kThreads) {
-      const int h = e / nt, t = ta + e % nt;
-      float zz = sm.coefc[h][0] * f16_value(c0row[t]);
-      for (int i = 0; i < nu; ++i) {
-        const int ch = sm.ulist[i];
-        zz = fmaf(sm.coefc[h][ch], tail[(size_t)(t & 31) * D + ch], zz);
-      }
-      sm.z[h][t - t_begin] = zz;
-    }
-  }
-  __syncthreads();
-
-  // ---------------------------------------------------------------- softmax
-  const int nv = t_end - t_begin;
-  const int nvp = (nv + kTile - 1) / kTile * kTile;
+    // ---- weighted sum of the value codes
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float mx = -INFINITY;
-    for (int t = tid; t < nv; t += kThreads) mx = fmaxf(mx, sm.z[h][t]);
-    mx = wave_max(mx);
-    if (lane == 0) sm.redm[h][wave] = mx;
-  }
-  __syncthreads();
-  float mrow[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float mx = sm.redm[h][0];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) mx = fmaxf(mx, sm.redm[h][w]);
-    mrow[h] = mx;
-    float ls = 0.0f;
-    for (int t = tid; t < nvp; t += kThreads) {
-      const float p = t < nv ? exp2f(sm.z[h][t] - mx) : 0.0f;
-      sm.z[h][t] = p;
-      ls += p;
-    }
-    ls = wave_sum(ls);
-    if (lane == 0) sm.redl[h][wave] = ls;
-  }
-  __syncthreads();
-
-  // ---------------------------------------------------------------- value pass
-  // rows G..2G-1 of my A buffer held low parts: clear them
-#pragma unroll
-  for (int kc = 0; kc < KCM; ++kc)
-    if (n16 >= G && n16 < 2 * G)
-      *reinterpret_cast<u32x4 *>(&sm.a[wave][kc][lane][0]) = u32x4{0u, 0u, 0u, 0u};
-  wave_sync();
-  const int jgrp = (wave * NTW * 16) / kGroup;   // value scale group of my channels
-  f32x4 vacc[NTW];
-#pragma unroll
-  for (int nt = 0; nt < NTW; ++nt) vacc[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  float spart[AREPV];
-#pragma unroll
-  for (int rep = 0; rep < AREPV; ++rep) spart[rep] = 0.0f;
-
-  for (int tile0 = t_begin; tile0 < t_end; tile0 += kTile) {
-    for (int e = tid; e < (kTile / 16) * (D / 4); e += kThreads) {
-      const int blk = e / (D / 4), c4 = e % (D / 4);
-      const int tokb = tile0 + 16 * blk;
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (tokb < t_end) w = *reinterpret_cast<const u32x4 *>(vwords + (size_t)(tokb >> 4) * D + 4 * c4);
-      *reinterpret_cast<u32x4 *>(&sm.st.v.w[blk][4 * c4]) = w;
-    }
-    {
-      const int t = tile0 + tid;
-#pragma unroll
-      for (int j = 0; j < VG; ++j)
-        sm.st.v.sig[tid][j] = t < t_end ? f16_value(vscales[(size_t)t * VG + j]) * fscale : 0.0f;
-    }
-    __syncthreads();
-#pragma unroll 1
-    for (int kc = 0; kc < kTile / 32; ++kc) {
-      const int kt0 = tile0 + 32 * kc;
-      if (kt0 >= t_end) break;   // uniform
-      // compact numerators: (head h, pair pi) -> A dword pi&3 of lane 16*(pi>>2) + h
-#pragma unroll
-      for (int rep = 0; rep < AREPV; ++rep) {
-        const int it = lane + 64 * rep;
-        if (it < 16 * G) {
-          const int h = it >> 4, pi = it & 15;
-          const int kgx = pi >> 2, ii = pi & 3;
-          const int r0 = 2 * (kgx & 1), d = ii & 1;
-          const int tl = 16 * (kgx >> 1) + (ii < 2 ? 4 + r0 + d : r0 + d);
-          const int zt = kt0 - t_begin;
-          const float p0 = sm.z[h][zt + tl] * sm.st.v.sig[32 * kc + tl][jgrp];
-          const float p1 = sm.z[h][zt + tl + 8] * sm.st.v.sig[32 * kc + tl + 8][jgrp];
-          const uint32_t pk = f16_pair(p0, p1);
-          spart[rep] += f16_low(pk) + f16_high(pk);
-          sm.a[wave][0][16 * kgx + h][ii] = pk;
-        }
-      }
-      wave_sync();
-      const u32x4 A = *reinterpret_cast<const u32x4 *>(&sm.a[wave][0][lane][0]);
-      const int blk = 2 * kc + (kg >> 1);
+    for (int kc2 = 0; kc2 < 2; ++kc2) {
+      const int blk = 2 * kc2 + (kg >> 1);
       const int r0 = 2 * (kg & 1);
 #pragma unroll
-      for (int nt = 0; nt < NTW; ++nt) {
-        const int ch = (wave * NTW + nt) * 16 + n16;
-        const uint32_t w = sm.st.v.w[blk][ch];
-        const u32x4 bv = {((w >> (2 * r0)) & kCode2) | kOne2, ((w >> (2 * r0 + 2)) & kCode2) | kOne2,
-                          ((w << (8 - 2 * r0)) & kCode2) | kOne2, ((w << (6 - 2 * r0)) & kCode2) | kOne2};
-        vacc[nt] = mfma16(A, bv, vacc[nt]);
+      for (int j = 0; j < K::VG; ++j) {
+        const u32x4 A = n16 < G ? *reinterpret_cast<const u32x4 *>(&W.abuf[4 * (((kc2 * K::VG + j) * 4 + kg) * G + n16)])
+                                : zero4;
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+          const int ch = 32 * j + 16 * t2 + n16;
+          const uint32_t w = W.u.st.vw[blk][ch];
+          const u32x4 bv = {((w >> (2 * r0)) & vmask) | vone, ((w >> (2 * r0 + 2)) & vmask) | vone,
+                            ((w << (8 - 2 * r0)) & vmask) | vone, ((w << (6 - 2 * r0)) & vmask) | vone};
+          vacc[2 * j + t2] = mfma16(A, bv, vacc[2 * j + t2]);
+        }
       }
-      wave_sync();
     }
-    __syncthreads();
+    wave_sync();
+    if (more) commit();
+    wave_sync();
   }
 
-  // ---------------------------------------------------------------- partials
-  float ssum[AREPV];
+  // ---------------------------------------------------------------- merge the wavefronts
+  {
+    float ssum[K::HS][K::VG];
 #pragma unroll
-  for (int rep = 0; rep < AREPV; ++rep) ssum[rep] = row16_sum(spart[rep]);
-  const float inv_f = 1.0f / fscale;
+    for (int hs = 0; hs < K::HS; ++hs)
 #pragma unroll
-  for (int nt = 0; nt < NTW; ++nt) {
-    const int ch = (wave * NTW + nt) * 16 + n16;
+      for (int j = 0; j < K::VG; ++j) ssum[hs][j] = row16_sum(spart[hs][j]);
+    const float inv_f = f_set ? ldexpf(1.0f, -f_run) : 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = 4 * kg + i;                    // C row of this register
-      // sum of the numerators of head h: lanes 16*(h%4).. of compact repeat h/4
-      const int hh = h < G ? h : 0;
-      float sh = 0.0f;
+    for (int nt = 0; nt < K::NTT; ++nt) {
+      const int ch = 16 * nt + n16;
 #pragma unroll
-      for (int rep = 0; rep < AREPV; ++rep) {
-        const float x = __shfl(ssum[rep], 16 * (hh % 4), 64);
-        if (rep == hh / 4) sh = x;
+      for (int i = 0; i < 4; ++i) {
+        const int h = 4 * kg + i;
+        const int hh = h < G ? h : 0;
+        float sh = 0.0f;
+#pragma unroll
+        for (int hs = 0; hs < K::HS; ++hs) {
+          const float x = __shfl(ssum[hs][nt / 2], 16 * (hh & 3), 64);   // value group of channel 16nt..
+          if (hs == hh / 4) sh = x;
+        }
+        if (h < G) W.u.merge[h][ch] = (8.0f * vacc[nt][i] - 11.0f * sh) * inv_f;
       }
-      if (h < G) wsp[h * (D + kPartialHead) + kPartialHead + ch] = (8.0f * vacc[nt][i] - 11.0f * sh) * inv_f;
     }
-  }
-  if (tid < G) {
-    float ls = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) ls += sm.redl[tid][w];
-    wsp[tid * (D + kPartialHead) + 0] = mrow[tid];
-    wsp[tid * (D + kPartialHead) + 1] = ls;
+    for (int h = 0; h < G; ++h)
+      if (lane == h) {
+        W.mstate[h] = m_run[h];
+        W.lstate[h] = l_run[h];
+      }
+  }
+  __syncthreads();
+  for (int e = tid; e < G * D; e += kThreads) {
+    const int h = e / D, ch = e % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+      if (sm.w[w].lstate[h] > 0.0f) M = fmaxf(M, sm.w[w].mstate[h]);
+    float o = 0.0f, L = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      if (sm.w[w].lstate[h] > 0.0f) {
+        const float f = exp2f(sm.w[w].mstate[h] - M);
+        o = fmaf(sm.w[w].u.merge[h][ch], f, o);
+        L = fmaf(sm.w[w].lstate[h], f, L);
+      }
+    }
+    wsp[h * (D + kPartialHead) + kPartialHead + ch] = o;
+    if (ch == 0) {
+      wsp[h * (D + kPartialHead) + 0] = M;
+      wsp[h * (D + kPartialHead) + 1] = L;
+    }
   }
 }
 

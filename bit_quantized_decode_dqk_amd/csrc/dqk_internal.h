@@ -15,10 +15,11 @@ constexpr int kDefaultSplit = 1024; // bf16 decode split length when the caller 
 constexpr int kMaxSplitTokensTimesG = 8192;
 inline int max_split_tokens(int group) { return kMaxSplitTokensTimesG / group; }
 
-// Default 2-bit decode split: aim at >= 512 work items (two per compute unit),
-// in 256-token steps, at most the LDS bound.
+// Default 2-bit decode split: about three resident workgroups per compute unit
+// (two for groups of 8) across 256 compute units, in 256-token steps, bounded.
 inline int default_decode_split(int group, int capacity, int units) {
-  const long long per = ((long long)capacity * units + 511) / 512;
+  const long long slots = (group == 8 ? 2 : 3) * 256LL;
+  const long long per = ((long long)capacity * units + slots - 1) / slots;
   int s = (int)((per + 255) / 256 * 256);
   if (s < 256) s = 256;
   const int mx = max_split_tokens(group);
