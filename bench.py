@@ -78,6 +78,85 @@ def append_bytes(batch: int, hkv: int, d: int, positions, in_bytes: int) -> int:
     return total
 
 
+# ----------------------------------------------------------------------------- profiles
+
+KERNEL_SOURCES = ("bit_quantized_decode_dqk_amd/csrc/dqk_decode.hip",
+                  "bit_quantized_decode_dqk_amd/csrc/dqk_combine.hip",
+                  "bit_quantized_decode_dqk_amd/csrc/dqk_internal.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_ctx128k_traffic.txt")
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per decode launch from the committed counter summary, or None when
+    the summary is absent or was taken on different kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    fields = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith((" ", "#")):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("source_hash") != kernel_source_hash():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def summarize_rocprof(directory: str, kernel_regex: str, copy_mib: int) -> None:
+    """Print a short text summary of rocprofv3 csv output under `directory`:
+    kernel statistics (--kernel-trace --stats) and, when present, per-dispatch
+    FETCH_SIZE / WRITE_SIZE of the kernels matching `kernel_regex`, with the
+    counter scaled by its reading on a plain copy of `copy_mib` MiB."""
+    import csv
+    import glob
+    import re
+    pat = re.compile(kernel_regex)
+    for path in sorted(glob.glob(os.path.join(directory, "**", "*kernel_stats.csv"), recursive=True)):
+        rows = list(csv.DictReader(open(path)))
+        print(f"kernel stats ({os.path.relpath(path, directory)}):")
+        print(f"  {'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9} {'pct':>6}  kernel")
+        for r in rows:
+            print(f"  {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f} "
+                  f"{float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f} "
+                  f"{float(r['Percentage']):6.2f}  {r['Name'][:110]}")
+    for path in sorted(glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)):
+        per = {}
+        names = {}
+        for r in csv.DictReader(open(path)):
+            key = int(r["Dispatch_Id"])
+            per.setdefault(key, {})
+            per[key][r["Counter_Name"]] = per[key].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            names[key] = r["Kernel_Name"]
+        counters = sorted({c for v in per.values() for c in v})
+        for cname in counters:
+            target = [per[k][cname] for k in sorted(per) if pat.search(names[k]) and cname in per[k]]
+            copies = [per[k][cname] for k in sorted(per)
+                      if "copy" in names[k].lower() and "elementwise" in names[k].lower() and cname in per[k]]
+            print(f"counter {cname} ({os.path.relpath(path, directory)}): "
+                  f"{len(target)} dispatches of /{kernel_regex}/")
+            if not target:
+                continue
+            avg = sum(target) / len(target)
+            print(f"  {cname}_avg_kib_per_dispatch: {avg:.1f}")
+            if copies and copy_mib > 0:
+                big = max(copies)
+                factor = copy_mib * 1024.0 / big
+                print(f"  copy_kernel_{cname}_kib: {big:.1f} for {copy_mib} MiB moved "
+                      f"(factor {factor:.4f} bytes per counted byte)")
+                print(f"  {cname}_bytes_per_dispatch_scaled: {avg * 1024.0 * factor:.0f}")
+
+
 # ----------------------------------------------------------------------------- CPU baseline
 
 def cpu_baseline(wl, a, b, keep, sm, budget_s: float = 20.0):
@@ -131,7 +210,17 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--split", type=int, default=0)
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="after the timed steps, copy this many MiB device to device "
+                         "(a known-size reference for HBM byte counters)")
+    ap.add_argument("--summarize-rocprof", metavar="DIR",
+                    help="print a summary of rocprofv3 csv output under DIR and exit")
+    ap.add_argument("--kernel-regex", default="decode_kernel")
     args = ap.parse_args()
+    if args.summarize_rocprof:
+        summarize_rocprof(args.summarize_rocprof, args.kernel_regex, args.calibrate_copy_mib)
+        print(f"source_hash: {kernel_source_hash()}")
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -231,6 +320,15 @@ def main():
         f"(p10 {np.percentile(dec_ms, 10) * 1e3:.1f} p90 {np.percentile(dec_ms, 90) * 1e3:.1f}), "
         f"append+select {np.mean(pre_ms) * 1e3:.1f} us, {gbs:.0f} GB/s step, {dec_gbs:.0f} GB/s decode")
 
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     extras = {}
     if not args.no_extras:
         extras = run_extras(M, torch, wl, caches, a_d, step_q, qp, idx, out, ws, k_d, v_d, sm,
@@ -256,7 +354,7 @@ def main():
                    "keep": keep, "cache_copies": args.copies},
         "tokens_per_s": round(wl.batch / (ms_step * 1e-3), 1),
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
                      "kernel": "pruned decode (partial + combine launches)",
                      "bytes_per_launch": int(np.mean([dec_bytes[i] for i in timed])),
                      "avg_us": round(dec_avg_ms * 1e3, 2)},

@@ -49,14 +49,8 @@ size_t ws_bytes_for(int batch, int hkv, int hq, int d, int tokens, int split) {
 }
 
 // Split of the 2-bit decode: the caller's, else the library's default.
-int decode_split(const dqk_cache *c, int hq, int split) {
-  const int group = hq / c->num_kv_heads;
-  return split != 0 ? split
-                    : dqk::default_decode_split(group, c->capacity, c->batch * c->num_kv_heads);
-}
-
-bool valid_decode_split(int hq, int hkv, int split) {
-  return valid_split(split) && split <= dqk::max_split_tokens(hq / hkv);
+int decode_split(const dqk_cache *c, int split) {
+  return split != 0 ? split : dqk::default_decode_split(c->capacity, c->batch * c->num_kv_heads);
 }
 
 }  // namespace
@@ -122,9 +116,9 @@ dqk_status dqk_decode_workspace_bytes(const dqk_cache *cache, int32_t hq, int32_
   dqk_status st = check_cache(cache);
   if (st != DQK_OK) return st;
   if (!supported_group(hq, cache->num_kv_heads)) return DQK_ERR_UNSUPPORTED;
-  if (!valid_decode_split(hq, cache->num_kv_heads, split)) return DQK_ERR_INVALID;
+  if (!valid_split(split)) return DQK_ERR_INVALID;
   *out = ws_bytes_for(cache->batch, cache->num_kv_heads, hq, cache->head_dim, cache->capacity,
-                      decode_split(cache, hq, split));
+                      decode_split(cache, split));
   return DQK_OK;
 }
 
@@ -141,8 +135,8 @@ dqk_status dqk_decode_attention(const dqk_cache *cache, const float *q_prime,
   }
   if (keep < 1 || keep > cache->head_dim) return DQK_ERR_INVALID;
   if (!isfinite(sm_scale)) return DQK_ERR_INVALID;
-  if (!valid_decode_split(hq, cache->num_kv_heads, split)) return DQK_ERR_INVALID;
-  const int sp = decode_split(cache, hq, split);
+  if (!valid_split(split)) return DQK_ERR_INVALID;
+  const int sp = decode_split(cache, split);
   const size_t need = ws_bytes_for(cache->batch, cache->num_kv_heads, hq, cache->head_dim,
                                    cache->capacity, sp);
   if (!workspace || ws_bytes < need || !aligned16(workspace)) return DQK_ERR_WORKSPACE;

@@ -173,8 +173,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(dqk_cache c,
   __shared__ Smem<D, G> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n16 = lane & 15, kg = lane >> 4;
-  const int item = blockIdx.x;
-  const int unit = item / nsplit, s = item % nsplit;
+  // Split-major order: the short last split of every sequence is launched last.
+  const int units = c.batch * c.num_kv_heads;
+  const int unit = blockIdx.x % units, s = blockIdx.x / units;
+  const int item = unit * nsplit + s;
   const int b = unit / c.num_kv_heads, g = unit % c.num_kv_heads;
   const int len = max(0, min(c.lengths[b], c.capacity));
   const int t_begin = s * split;

@@ -11,19 +11,15 @@ namespace dqk {
 constexpr int kGroup = 32;          // tokens (keys) or channels (values) per scale
 constexpr int kDefaultSplit = 1024; // bf16 decode split length when the caller passes 0
 
-// 2-bit decode: a split's logits live in LDS, G * split <= kMaxSplitTokensTimesG.
-constexpr int kMaxSplitTokensTimesG = 8192;
-inline int max_split_tokens(int group) { return kMaxSplitTokensTimesG / group; }
-
-// Default 2-bit decode split: about three resident workgroups per compute unit
-// (two for groups of 8) across 256 compute units, in 256-token steps, bounded.
-inline int default_decode_split(int group, int capacity, int units) {
-  const long long slots = (group == 8 ? 2 : 3) * 256LL;
-  const long long per = ((long long)capacity * units + slots - 1) / slots;
-  int s = (int)((per + 255) / 256 * 256);
-  if (s < 256) s = 256;
-  const int mx = max_split_tokens(group);
-  return s > mx ? mx : s;
+// Default 2-bit decode split: the capacity spread over about two resident
+// workgroups per compute unit on 256 compute units, rounded down to 256-token
+// steps (at least 256).  Rounding down keeps every full split inside the first
+// wave of workgroups; the short last split of each sequence is launched last.
+inline int default_decode_split(int capacity, int units) {
+  const long long slots = 2 * 256LL;
+  const long long per = ((long long)capacity * units) / slots;
+  const int s = (int)(per / 256 * 256);
+  return s < 256 ? 256 : s;
 }
 
 // fp32 -> binary16 bits: round to nearest even (the hardware conversion), with

@@ -79,9 +79,11 @@ const char *dqk_status_str(dqk_status s);
 dqk_status dqk_cache_plane_bytes(int32_t batch, int32_t num_kv_heads, int32_t head_dim,
                                  int32_t capacity, size_t *out_bytes);
 
-/* Append step ("every token adds new keys and values that must be kept for later
- * attention steps"; key transform from "paired transforms"; 2-bit storage from
- * "Quantization cuts storage to 2 bits per value"; channel-0 protection).
+/* Append step: each generated token's key and value join the cache for all later
+ * decode steps (tech.dede.sh summary, "Why the cache becomes a bottleneck"); the
+ * key goes through the key transform ("Paired transforms instead of shared
+ * rotation"), keys and values are stored in 2 bits ("Throughput on SGLang"), and
+ * channel 0 is protected (arXiv abstract).
  * For each batch row b, n = min(n_new[b], max_new, capacity - lengths[b]) tokens
  * k_new[b][g][i][:], v_new[b][g][i][:] (i < n) are stored at positions
  * lengths[b]..lengths[b]+n-1 of every KV head g, then lengths[b] += n:
@@ -98,9 +100,10 @@ dqk_status dqk_transform_quantize_append(const dqk_cache *cache, const void *k_n
                                          const float *bmat, const int32_t *n_new,
                                          int32_t max_new, dqk_stream_t stream);
 
-/* Query transform and channel selection ("the query transform sharpens the
- * distribution for pruning"; "dynamic channel pruning" at a query-channel
- * sparsity).  For each (b, query head h), with KV head g = h / (hq/hkv):
+/* Query transform and channel selection: the query transform concentrates query
+ * energy in few channels so that the rest can be dropped per query (tech.dede.sh
+ * summary, "Paired transforms instead of shared rotation"; arXiv abstract,
+ * dynamic channel pruning at a query-channel sparsity).  For each (b, query head h), with KV head g = h / (hq/hkv):
  * q' = q A_g (same FMA chain as above), written to q_prime; sel_idx receives, in
  * ascending order, channel 0 plus the keep-1 channels c >= 1 of largest |q'_c|,
  * equal magnitudes going to the lower index.
@@ -116,15 +119,14 @@ dqk_status dqk_select_channels(const void *q, dqk_dtype dtype, const float *amat
 dqk_status dqk_decode_workspace_bytes(const dqk_cache *cache, int32_t hq,
                                       int32_t split_tokens, size_t *out_bytes);
 
-/* Decode attention over the stored cache ("pruning removes ... key channels from
- * reads"; values are never pruned).  For each (b, h) with T = lengths[b]:
+/* Decode attention over the stored cache: the key channels a head does not keep
+ * are never read from HBM; values are never pruned.  For each (b, h) with T = lengths[b]:
  *   z_t = sm_scale * sum_{c in sel_idx[b][h]} q'_c k~_{t,c}
  *   out[b][h] = sum_t softmax(z)_t v~_t        (T = 0 gives zeros)
  * where k~ is channel 0's fp16 value, the 2-bit value of complete groups, or the
  * exact tail.  Only the kept key channels' codes and scales are read from HBM.
- * The sequence is split into chunks of split_tokens (a multiple of 32 and at
- * most 8192/(hq/hkv); 0 = the library's choice) reduced with an online-max
- * combine.  Products run on the matrix cores with fp32 accumulation.
+ * The sequence is split into chunks of split_tokens (a positive multiple of 32;
+ * 0 = the library's choice) reduced with an online-max combine.  Products run on the matrix cores with fp32 accumulation.
  * q_prime: [batch][hq][d] fp32; sel_idx: [batch][hq][keep] as produced by
  * dqk_select_channels; out: [batch][hq][d] fp32; workspace: device scratch of at
  * least dqk_decode_workspace_bytes (contents need no initialization). */

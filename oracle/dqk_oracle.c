@@ -78,8 +78,8 @@ void dqko_f32_from_f16_n(const uint16_t *h, size_t n, float *out)
 /* ------------------------------------------------------------- transform */
 
 /* Paired transforms act on row vectors: q' = q A, k' = k B with A B^T = I
- * (the abstract's "paired non-orthogonal query and key transforms" that keep
- * query-key dot products).  Reading: fp32, one fused multiply-add chain per
+ * (arXiv abstract: a query transform and a key transform that are not
+ * orthogonal and come as a pair, so that query-key dot products survive).  Reading: fp32, one fused multiply-add chain per
  * output over the input index in ascending order, starting from +0. */
 void dqko_transform(const float *x, const float *m, int d, float *y)
 {
@@ -92,8 +92,8 @@ void dqko_transform(const float *x, const float *m, int d, float *y)
 
 /* ------------------------------------------------------------- quantizer */
 
-/* INT2 with an fp16 scale per group of 32 ("Quantization cuts storage to 2 bits
- * per value").  Reading: symmetric four-level grid s*{-3,-1,1,3}, s = fp16 of
+/* INT2 with an fp16 scale per group of 32 (tech.dede.sh summary, "Throughput on
+ * SGLang": two bits per stored value).  Reading: symmetric four-level grid s*{-3,-1,1,3}, s = fp16 of
  * max|x|/3 (one correctly rounded fp32 division), no zero point; a value goes
  * to the level whose decision interval holds it, thresholds -2s, 0, 2s, a value
  * on a threshold going up. */
@@ -232,8 +232,8 @@ static float value_value(const dqko_cache *c, int b, int g, int t, int ch)
 
 /* ------------------------------------------------------------- append */
 
-/* "Every token adds new keys and values that must be kept for later attention
- * steps."  Per new token at position p: k' = k B; channel 0 of k' to fp16;
+/* Each generated token's key and value stay in the cache for every later step
+ * (tech.dede.sh summary, "Why the cache becomes a bottleneck").  Per new token at position p: k' = k B; channel 0 of k' to fp16;
  * k' into tail row p mod 32; when p closes a 32-token group, channels 1..d-1 of
  * the 32 tail rows are quantized per channel.  Values are quantized per token in
  * groups of 32 channels at once. */

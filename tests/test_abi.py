@@ -73,8 +73,9 @@ def test_cache_validation_without_gpu():
     assert L.dqk_decode_workspace_bytes(C.byref(fake_cache()), 6, 0, C.byref(out)) == UNSUPPORTED
     assert L.dqk_decode_workspace_bytes(C.byref(fake_cache()), 8, 48, C.byref(out)) == INVALID
     assert L.dqk_decode_workspace_bytes(C.byref(fake_cache()), 8, 2048, C.byref(out)) == OK
-    assert L.dqk_decode_workspace_bytes(C.byref(fake_cache()), 8, 2080, C.byref(out)) == INVALID
-    assert L.dqk_decode_workspace_bytes(C.byref(fake_cache()), 16, 1056, C.byref(out)) == INVALID
+    assert out.value == 2 * 2 * 1 * 4 * 132 * 4          # one split longer than the capacity
+    assert L.dqk_decode_workspace_bytes(C.byref(fake_cache()), 8, -32, C.byref(out)) == INVALID
+    assert L.dqk_decode_workspace_bytes(C.byref(fake_cache()), 16, 1056, C.byref(out)) == OK
     assert L.dqk_decode_workspace_bytes(None, 8, 0, C.byref(out)) == INVALID
 
 
