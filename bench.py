@@ -142,7 +142,7 @@ def summarize_rocprof(directory: str, kernel_regex: str, copy_mib: int) -> None:
         for cname in counters:
             target = [per[k][cname] for k in sorted(per) if pat.search(names[k]) and cname in per[k]]
             copies = [per[k][cname] for k in sorted(per)
-                      if "copy" in names[k].lower() and "elementwise" in names[k].lower() and cname in per[k]]
+                      if "copybuffer" in names[k].lower() and cname in per[k]]
             print(f"counter {cname} ({os.path.relpath(path, directory)}): "
                   f"{len(target)} dispatches of /{kernel_regex}/")
             if not target:

@@ -27,6 +27,7 @@ SOURCES = {
     "dqk_select.hip": ["-ffp-contract=off"],
     "dqk_dequant.hip": ["-ffp-contract=off"],
     "dqk_decode.hip": ["-fno-honor-nans"],   # inputs are finite; only -inf is used
+    "dqk_decode4.hip": ["-fno-honor-nans"],
     "dqk_bf16.hip": [],
     "dqk_combine.hip": [],
 }

@@ -49,8 +49,11 @@ size_t ws_bytes_for(int batch, int hkv, int hq, int d, int tokens, int split) {
 }
 
 // Split of the 2-bit decode: the caller's, else the library's default.
-int decode_split(const dqk_cache *c, int split) {
-  return split != 0 ? split : dqk::default_decode_split(c->capacity, c->batch * c->num_kv_heads);
+int decode_split(const dqk_cache *c, int hq, int split) {
+  if (split != 0) return split;
+  const int units = c->batch * c->num_kv_heads;
+  return hq == 4 * c->num_kv_heads ? dqk::balanced_decode_split(c->capacity, units)
+                                   : dqk::default_decode_split(c->capacity, units);
 }
 
 }  // namespace
@@ -118,7 +121,7 @@ dqk_status dqk_decode_workspace_bytes(const dqk_cache *cache, int32_t hq, int32_
   if (!supported_group(hq, cache->num_kv_heads)) return DQK_ERR_UNSUPPORTED;
   if (!valid_split(split)) return DQK_ERR_INVALID;
   *out = ws_bytes_for(cache->batch, cache->num_kv_heads, hq, cache->head_dim, cache->capacity,
-                      decode_split(cache, split));
+                      decode_split(cache, hq, split));
   return DQK_OK;
 }
 
@@ -136,7 +139,7 @@ dqk_status dqk_decode_attention(const dqk_cache *cache, const float *q_prime,
   if (keep < 1 || keep > cache->head_dim) return DQK_ERR_INVALID;
   if (!isfinite(sm_scale)) return DQK_ERR_INVALID;
   if (!valid_split(split)) return DQK_ERR_INVALID;
-  const int sp = decode_split(cache, split);
+  const int sp = decode_split(cache, hq, split);
   const size_t need = ws_bytes_for(cache->batch, cache->num_kv_heads, hq, cache->head_dim,
                                    cache->capacity, sp);
   if (!workspace || ws_bytes < need || !aligned16(workspace)) return DQK_ERR_WORKSPACE;

@@ -34,84 +34,17 @@
 // MFMA layout.  Values: each wavefront owns d/4 output channels.  The partial
 // (max, sum, output) of every head goes to the workspace for the combine.
 #include "dqk_internal.h"
+#include "dqk_wave.h"
 
 namespace dqk {
 namespace {
 
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+using namespace wave;
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kTile = 256;                      // tokens staged per tile
-constexpr int kTileGroups = kTile / kGroup;     // 8 key groups per tile
 constexpr uint32_t kOne2 = 0x3C003C00u;         // two fp16 1.0 (code 0)
 constexpr uint32_t kCode2 = 0x03000300u;        // code bits -> fp16 mantissa bits 8..9
-
-__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a),
-                                                __builtin_bit_cast(half8, b), c, 0, 0, 0);
-}
-
-__device__ __forceinline__ uint32_t f16_pair(float lo, float hi) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
-}
-__device__ __forceinline__ float f16_low(uint32_t w) {
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
-}
-__device__ __forceinline__ float f16_high(uint32_t w) {
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
-}
-
-// Order LDS traffic between lanes of one wavefront (no workgroup barrier).
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-}
-
-// Cross-lane reductions with DPP moves (no LDS traffic).  `idn` fills lanes the
-// move does not write, so it must be the identity of the operation.
-template <int CTRL, int ROWS = 0xf>
-__device__ __forceinline__ float dpp_mov(float idn, float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, idn),
-                                                              __builtin_bit_cast(int, v), CTRL,
-                                                              ROWS, 0xf, false));
-}
-__device__ __forceinline__ float row16_max(float x) {   // every lane: max over its 16-lane row
-  x = fmaxf(x, dpp_mov<0xB1>(x, x));   // quad_perm [1,0,3,2]  (max is idempotent: fill = x)
-  x = fmaxf(x, dpp_mov<0x4E>(x, x));   // quad_perm [2,3,0,1]
-  x = fmaxf(x, dpp_mov<0x141>(x, x));  // row_half_mirror
-  x = fmaxf(x, dpp_mov<0x140>(x, x));  // row_mirror
-  return x;
-}
-__device__ __forceinline__ float row16_sum(float x) {   // every lane: sum over its 16-lane row
-  x += dpp_mov<0xB1>(0.0f, x);
-  x += dpp_mov<0x4E>(0.0f, x);
-  x += dpp_mov<0x141>(0.0f, x);
-  x += dpp_mov<0x140>(0.0f, x);
-  return x;
-}
-__device__ __forceinline__ float wave_max(float x) {    // uniform result
-  x = row16_max(x);
-  x = fmaxf(x, dpp_mov<0x142, 0xa>(x, x));  // row_bcast:15
-  x = fmaxf(x, dpp_mov<0x143, 0xc>(x, x));  // row_bcast:31
-  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
-}
-__device__ __forceinline__ float wave_sum(float x) {    // uniform result
-  x = row16_sum(x);
-  x += dpp_mov<0x142, 0xa>(0.0f, x);
-  x += dpp_mov<0x143, 0xc>(0.0f, x);
-  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
-}
-
-// Keeps a constant in a VGPR so (x & m) | c selects one v_and_or_b32 (gfx9 VOP3
-// takes no literals and at most one scalar operand).
-__device__ __forceinline__ uint32_t in_vgpr(uint32_t v) {
-  asm volatile("" : "+v"(v));
-  return v;
-}
 
 constexpr int kTok = 64;   // tokens per wavefront tile (two key groups)
 constexpr int kYRow = kTok / 4 * 2 + 8;   // dwords per channel octet in the key staging, padded
@@ -134,7 +67,7 @@ struct Cfg {
 };
 
 template <int D, int G>
-struct WaveSmem {
+struct __attribute__((aligned(16))) WaveSmem {
   union {
     struct {
       uint32_t y[D / 8][kYRow];        // key codes: channel octet, (token quad, 4 ch + 4 ch), padded
@@ -151,7 +84,7 @@ struct WaveSmem {
 };
 
 template <int D, int G>
-struct Smem {
+struct __attribute__((aligned(16))) Smem {
   WaveSmem<D, G> w[kWaves];
   float coefc[G][D];                   // q' * sm * log2(e) by channel (0 if dropped)
   float coefs[G][D];                   // coefc in U order * 2^-E_h (0 past |U|)
@@ -651,7 +584,12 @@ hipError_t launch_decode_d(const dqk_cache &c, const float *qp, const int32_t *s
   switch (hq / c.num_kv_heads) {
     case 1: return launch_decode_t<D, 1>(c, qp, sel, hq, keep, scale2, split, out, ws, s);
     case 2: return launch_decode_t<D, 2>(c, qp, sel, hq, keep, scale2, split, out, ws, s);
-    case 4: return launch_decode_t<D, 4>(c, qp, sel, hq, keep, scale2, split, out, ws, s);
+    case 4: {
+      const int nsplit = num_splits(c.capacity, split);
+      const hipError_t e = launch_decode4(c, qp, sel, hq, keep, scale2, nsplit, ws, s);
+      if (e != hipSuccess) return e;
+      return launch_combine(ws, c.batch, hq, c.num_kv_heads, D, nsplit, out, s);
+    }
     default: return launch_decode_t<D, 8>(c, qp, sel, hq, keep, scale2, split, out, ws, s);
   }
 }

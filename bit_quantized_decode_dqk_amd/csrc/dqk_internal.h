@@ -15,6 +15,19 @@ constexpr int kDefaultSplit = 1024; // bf16 decode split length when the caller 
 // workgroups per compute unit on 256 compute units, rounded down to 256-token
 // steps (at least 256).  Rounding down keeps every full split inside the first
 // wave of workgroups; the short last split of each sequence is launched last.
+// Groups of four query heads share the sequence by length (each workgroup takes
+// an equal share of the current tokens): the default only fixes the number of
+// splits, about two workgroups per compute unit, with at least 256 tokens of
+// capacity per split.
+inline int balanced_decode_split(int capacity, int units) {
+  int nsplit = 512 / units;
+  if (nsplit < 1) nsplit = 1;
+  const int most = (capacity + 255) / 256;
+  if (nsplit > most) nsplit = most;
+  const int split = (capacity + nsplit - 1) / nsplit;
+  return (split + 31) / 32 * 32;
+}
+
 inline int default_decode_split(int capacity, int units) {
   const long long slots = 2 * 256LL;
   const long long per = ((long long)capacity * units) / slots;
@@ -63,6 +76,8 @@ hipError_t launch_select(const void *q, bool bf16, const float *amat, int batch,
 hipError_t launch_decode(const dqk_cache &c, const float *q_prime, const int32_t *sel_idx, int hq,
                          int keep, float sm_scale, int split, float *out, float *ws,
                          hipStream_t s);
+hipError_t launch_decode4(const dqk_cache &c, const float *q_prime, const int32_t *sel_idx, int hq,
+                          int keep, float scale2, int nsplit, float *ws, hipStream_t s);
 hipError_t launch_dequant(const dqk_cache &c, float *k_out, float *v_out, hipStream_t s);
 hipError_t launch_bf16_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                               const int32_t *lengths, int batch, int hq, int hkv, int d, int ld_t,

@@ -195,10 +195,14 @@ def test_decode_ragged_edges(orc):
         assert not out[0].any()
 
 
-@pytest.mark.parametrize("hq,hkv,d", [(1, 1, 64), (2, 1, 64), (8, 1, 64), (4, 2, 128),
-                                      (16, 2, 128), (64, 8, 128)])
-def test_decode_group_sizes(orc, hq, hkv, d):
-    wl = W.custom(f"g{hq}-{hkv}-{d}", 25, 2, hq, hkv, d, [700, 1333], 1344, "bf16",
+@pytest.mark.parametrize("hq,hkv,d,cap", [(1, 1, 64, 1344), (2, 1, 64, 1344), (8, 1, 64, 1344),
+                                          (4, 2, 128, 1344), (16, 2, 128, 1344),
+                                          (64, 8, 128, 1344), (4, 1, 64, 1344), (8, 2, 64, 1376),
+                                          (4, 1, 128, 1376), (8, 2, 128, 1344)])
+def test_decode_group_sizes(orc, hq, hkv, d, cap):
+    """Every GQA group size and head dimension; groups of four run the dedicated
+    kernel, with capacities that are and are not multiples of 64 tokens."""
+    wl = W.custom(f"g{hq}-{hkv}-{d}", 25, 2, hq, hkv, d, [700, min(1333, cap - 11)], cap, "bf16",
                   log_uniform_key_scales=True, student_t_queries=(hq == 64))
     decode_case(orc, wl, splits=(0, 128))
     decode_case(orc, wl, sm_mult=0.02, splits=(0,))
