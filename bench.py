@@ -81,7 +81,9 @@ def append_bytes(batch: int, hkv: int, d: int, positions, in_bytes: int) -> int:
 # ----------------------------------------------------------------------------- profiles
 
 KERNEL_SOURCES = ("bit_quantized_decode_dqk_amd/csrc/dqk_decode.hip",
+                  "bit_quantized_decode_dqk_amd/csrc/dqk_decode4.hip",
                   "bit_quantized_decode_dqk_amd/csrc/dqk_combine.hip",
+                  "bit_quantized_decode_dqk_amd/csrc/dqk_wave.h",
                   "bit_quantized_decode_dqk_amd/csrc/dqk_internal.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_ctx128k_traffic.txt")
 
