@@ -585,6 +585,8 @@ hipError_t launch_decode_d(const dqk_cache &c, const float *qp, const int32_t *s
     case 1: return launch_decode_t<D, 1>(c, qp, sel, hq, keep, scale2, split, out, ws, s);
     case 2: return launch_decode_t<D, 2>(c, qp, sel, hq, keep, scale2, split, out, ws, s);
     case 4: {
+      if (!decode4_supported(c))
+        return launch_decode_t<D, 4>(c, qp, sel, hq, keep, scale2, split, out, ws, s);
       const int nsplit = num_splits(c.capacity, split);
       const hipError_t e = launch_decode4(c, qp, sel, hq, keep, scale2, nsplit, ws, s);
       if (e != hipSuccess) return e;

@@ -76,6 +76,7 @@ hipError_t launch_select(const void *q, bool bf16, const float *amat, int batch,
 hipError_t launch_decode(const dqk_cache &c, const float *q_prime, const int32_t *sel_idx, int hq,
                          int keep, float sm_scale, int split, float *out, float *ws,
                          hipStream_t s);
+bool decode4_supported(const dqk_cache &c);
 hipError_t launch_decode4(const dqk_cache &c, const float *q_prime, const int32_t *sel_idx, int hq,
                           int keep, float scale2, int nsplit, float *ws, hipStream_t s);
 hipError_t launch_dequant(const dqk_cache &c, float *k_out, float *v_out, hipStream_t s);

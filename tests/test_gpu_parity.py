@@ -208,6 +208,20 @@ def test_decode_group_sizes(orc, hq, hkv, d, cap):
     decode_case(orc, wl, sm_mult=0.02, splits=(0,))
 
 
+@pytest.mark.parametrize("d,lens,cap", [(128, [5000, 2049, 257], 5056), (64, [3000, 1, 700], 3008),
+                                         (128, [4096, 4095, 31], 4096)])
+def test_decode_group4_many_blocks(orc, d, lens, cap):
+    """Groups of four with capacities that are multiples of 64 (the dedicated
+    kernel): several 256-token blocks per workgroup, an odd block count, ragged
+    rows, the exact tail, a row shorter than one key group, and split counts from
+    one to more than the blocks."""
+    wl = W.custom(f"g4-{d}", 27, len(lens), 32, 8, d, lens, cap, "bf16",
+                  log_uniform_key_scales=True)
+    decode_case(orc, wl, splits=(0, 64, 512, 1024, cap))
+    decode_case(orc, wl, sparsity=0, sm_mult=0.02, splits=(0, 256))
+    decode_case(orc, wl, sparsity=60, sm_mult=0.05, splits=(0,))
+
+
 def test_decode_poisoned_dropped_channels(orc):
     """Codes and scales of channels no head of the group keeps are overwritten
     with 0xFF / fp16 NaN: the output is bitwise unchanged, so they are never used."""
