@@ -11,22 +11,25 @@
 // last group, the exact tail.  Each head's logit uses only its own channels (its
 // coefficient is zero on the others).  Values are never pruned.
 //
-// Memory pipeline.  A block is 256 tokens of one (batch row, KV head): the key
-// code rows of U, their scales, channel 0, the value words and the value
-// scales, about 20 KB at head_dim 128.  Every lane of the workgroup issues the
-// same fixed set of buffer loads for a block (lanes without a part of it point
-// past the plane, which returns zero and moves no bytes); two blocks are in
-// flight in registers while a third is computed from LDS.  A block's registers
-// are written to one of two LDS buffers (key codes transposed into the operand
-// order of the logit product) and one workgroup barrier per block publishes it.
-// Wavefront w then computes the block's 64-token tile w.
+// Two passes per chunk of up to eight blocks (2048 tokens):
+//  1. keys.  Every lane of the workgroup issues the same fixed set of buffer
+//     loads for a block (lanes without a part of it point past the plane, which
+//     returns zero and moves no bytes); two blocks are in flight in registers
+//     while a third is worked on.  A block's key codes are written to one of two
+//     LDS buffers, transposed into the operand order of the logit product, and
+//     one workgroup barrier per block publishes them.  Wavefront w computes the
+//     logits of the block's 64-token tile w and keeps them in registers.
+//  2. values.  With the exact maximum of its logits in the chunk known, every
+//     wavefront streams the value words and scales of its own tiles straight
+//     into registers (two tiles in flight, no barrier) and accumulates the
+//     weighted sum.  Only a later chunk with a larger maximum rescales what was
+//     accumulated.
 //
 // Decoding.  A 2-bit code u whose bit pair sits at bits 2k, 2k+1 of an fp16 word
 // with a zero exponent field is the subnormal u * 2^(2k-24), exact; masking a
-// packed code word therefore yields two operands per instruction with no shift
-// and no offset, and the power 2^(2k-24) is compensated in the other operand or
-// in the output.  The matrix cores take fp16 subnormals as they are.  With the
-// level 2u - 3 of a code:
+// packed code word therefore yields two operands per instruction, and the power
+// 2^(2k-24) is compensated in the other operand or in the output.  The matrix
+// cores take fp16 subnormals as they are.  With the level 2u - 3 of a code:
 //  - logits, per 64-token tile with key groups g = 0, 1: A[(g, h, limb)][(g, s)]
 //    is the fp16 high or low part of q'_{h,U[s]} * sm * log2(e) * scale_{U[s],g}
 //    * 2^-E_h, block diagonal over g (rows 8g + 2h + limb, K = 16 union slots of
@@ -34,13 +37,11 @@
 //    shifted to mantissa bits 6-9 first); a product with B = 1 gives C1 = sum A.
 //    Then z = 2^(E_h + 25 - 2k) (C_high + C_low) - 3 2^E_h (C1_high + C1_low) + ch0 term.
 //  - values, per 32 tokens and 16 channels of value group j: A[h][t] =
-//    p_{h,t} scale_{t,j} 2^(F + 24 - 2k(t)) in fp16 (p the softmax numerator, F a
-//    power of two that keeps A finite), B[t][c] = u 2^(2k-24); a product with
-//    B = 2^(2k-24) gives S = 2^F sum p scale, and out = 2^-F (2 C - 3 S).
-// Softmax: each wavefront keeps a running maximum per head that may trail the
-// largest logit seen by up to 8 (log2 units); it moves, and the running sums
-// are rescaled, only when a logit exceeds it by more than that or a value scale
-// outgrows the range that 2^F allows.
+//    p_{h,t} scale_{t,j} 2^(F + 24 - 2k(t)) in fp16 (p = 2^(z - max) <= 1, F a
+//    power of two that keeps A below 2^15), B[t][c] = u 2^(2k-24); a product
+//    with B = 2^(2k-24) gives S = 2^F sum p scale, and out = 2^-F (2 C - 3 S).
+//    F moves (and what was accumulated is rescaled by a power of two) only when
+//    a value scale outgrows the range it allows.
 //
 // The capacity must be a multiple of 64 tokens (the key scales of a block are
 // then whole dwords of every scale row); other capacities use the general
@@ -62,7 +63,7 @@ constexpr int kWaves4 = kThreads4 / 64;
 constexpr int kTile4 = 64;          // tokens per wavefront tile: two key groups
 constexpr int kBlock4 = kTile4 * kWaves4;   // tokens per workgroup block
 constexpr int kKsPerBlock = kBlock4 / kGroup;   // key groups per block
-constexpr float kSlack = 8.0f;      // log2 headroom of the running maximum
+constexpr int kChunk4 = 8;          // blocks per chunk: logits of a chunk stay in registers
 constexpr uint32_t kOneF16x2 = 0x3C003C00u;
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit elements, range-checked (gfx9)
 constexpr uint32_t kFar = 0x40000000u;   // offset past every plane: the load returns zero
@@ -74,31 +75,21 @@ struct Lay4 {
   static constexpr int VG = D / 32;     // value scale groups
   static constexpr int SPL = D / 8;     // union slots per lane in the logit A build
   static constexpr int AROW = D + 8;    // fp16 per logit A row (padded against bank conflicts)
-  static constexpr int VCH = 4 * D;     // 16-byte value chunks per block (16 rows of D words)
-  static constexpr int SCH = D;         // 16-byte value-scale chunks per block
   static constexpr int KSD = D / 64;    // key-scale dwords per lane per block (4 per slot)
+  static constexpr int NH = D / 64;     // 64-channel halves of the weighted sum
 };
 
-// One 256-token block as staged in LDS.
+// The keys of one 256-token block as staged in LDS.
 template <int D>
-struct __attribute__((aligned(16))) Block4 {
+struct __attribute__((aligned(16))) KBlock4 {
   uint32_t y[kWaves4][Lay4<D>::OCT][16][2];   // key codes: tile, slot octet, token quad, slots 0-3 | 4-7
   uint16_t ksig[kKsPerBlock][D];              // key scales (fp16 bits): key group of the block, slot
-  uint32_t vw[16][D];                         // value words: 16-token row of the block, channel
-  // 16-byte chunk i of this region is written by lane i: the value scales (fp16
-  // bits, [token][value group]), then key channel 0 (fp16 bits), then chunks no
-  // part of the block needs (lanes without such a part write there)
-  union {
-    u32x4 chunk[kThreads4];
-    struct {
-      uint16_t vs[kBlock4][Lay4<D>::VG];
-      uint16_t c0[kBlock4];
-    } m;
-  } misc;
+  uint32_t c0w[kThreads4];                    // key channel 0: fp16 pair of tokens 2i, 2i+1 (i < 128)
 };
 
 template <int D>
 struct __attribute__((aligned(16))) WaveSmem4 {
+  u32x4 zero;   // a 16-byte zero operand
   union {
     struct {
       uint16_t abuf[16][Lay4<D>::AROW];           // logit A rows 8g+2h+limb, slots in octet order 0,2,1,3,4,6,5,7
@@ -111,25 +102,34 @@ struct __attribute__((aligned(16))) WaveSmem4 {
 
 template <int D>
 struct __attribute__((aligned(16))) Smem4 {
-  Block4<D> blk[2];
+  KBlock4<D> kb[2];
   WaveSmem4<D> w[kWaves4];
   float coefc[kG4][D];     // q' * sm * log2(e) by channel (0 where the head drops the channel)
   float coefs[kG4][D];     // coefc in union-slot order * 2^-E_h (0 past |U|)
   float e2[kG4];           // 2^E_h
-  float redm[kG4][kWaves4];
-  int hmask[D];
+  float redm[kG4][2];         // largest |coefficient| per head and 64-channel half
+  float tailz[kG4][kGroup];   // exact logits of the unfinished last key group
+  union {
+    uint8_t b[kG4][D];        // kept[h][c]: head h keeps channel c
+    uint32_t w[kG4 * D / 4];
+  } kept;
   int16_t ulist[D];
   int wcount[2];
 };
 
-// Registers of one block in flight.
+// Registers of one block of keys in flight.
 template <int D>
-struct Stage4 {
-  uint32_t kc[8];          // key codes: 8 slots x 16 tokens
-  u32x4 vw[2];             // value words: two 16-byte chunks
-  u32x4 vs;                // value scales: one 16-byte chunk
-  uint32_t ks[Lay4<D>::KSD];       // key scales: dwords (two groups of one slot each)
-  u32x4 c0;                // channel 0: one 16-byte chunk
+struct KStage4 {
+  uint32_t kc[8];              // key codes: 8 slots x 16 tokens
+  uint32_t ks[Lay4<D>::KSD];   // key scales: dwords (two groups of one slot each)
+  uint32_t c0;                 // channel 0: two tokens
+};
+
+// Registers of one tile of values in flight (one wavefront).
+template <int D>
+struct VStage4 {
+  uint32_t vw[Lay4<D>::NH][4];   // value words of channel 64 half + 16q + n, word rows 0-3 of the tile
+  uint32_t vs[Lay4<D>::VG];      // value scales of tokens t, t+1: [t groups | t+1 groups]
 };
 
 __device__ __forceinline__ float h2f(uint32_t bits16) {
@@ -193,6 +193,13 @@ __device__ __forceinline__ uint32_t reshi(uint32_t d, float a, uint32_t s, uint3
   return d;
 }
 
+// acc + (fp16 in the low half of h) * k, one mixed-precision FMA.
+__device__ __forceinline__ float mix_acc(float acc, uint32_t h, float k) {
+  float d;
+  asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[1,0,0]" : "=v"(d) : "v"(h), "v"(k), "v"(acc));
+  return d;
+}
+
 // Shift both 16-bit halves of x left / right by the amounts in the halves of s.
 __device__ __forceinline__ uint32_t pk_shl16(uint32_t x, uint32_t s) {
   uint32_t d;
@@ -231,9 +238,6 @@ __device__ __forceinline__ void block_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// KSP: 2-byte loads are not needed for the key scales of a block (a key scale row
-// starts on a dword boundary).  The kernel is only launched with capacity % 64 == 0,
-// where this holds; KSP=false loads the scales as 16-bit halves.
 template <int D>
 __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
                                                                const float *__restrict__ qp,
@@ -248,6 +252,18 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
   const int units = c.batch * c.num_kv_heads;
   const int unit = blockIdx.x % units, s = blockIdx.x / units;
   const int b = unit / c.num_kv_heads, g = unit % c.num_kv_heads;
+  // The group's q' rows (all channels) and kept-channel lists are loaded before
+  // anything waits, in parallel with the length: one round trip for the setup.
+  const size_t row0 = (size_t)b * hq + (size_t)g * G;
+  constexpr int SJ = (G * D) / kThreads4;   // elements per lane
+  float qv[SJ];
+  int sv[SJ];
+#pragma unroll
+  for (int k = 0; k < SJ; ++k) {
+    const int e = tid + kThreads4 * k;
+    qv[k] = qp[row0 * D + e];
+    sv[k] = e < G * keep ? sel[row0 * keep + e] : -1;
+  }
   const int len = max(0, min(c.lengths[b], c.capacity));
   const int nblk_all = (len + kBlock4 - 1) / kBlock4;
   const int blo = (int)(((long long)s * nblk_all) / nsplit);
@@ -274,29 +290,28 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
   const int code_end = min(t_body, t_end);
 
   // ---------------------------------------------------------------- setup (whole workgroup)
-  for (int e = tid; e < G * D; e += kThreads4) sm.coefc[e / D][e % D] = 0.0f;
-  for (int e = tid; e < D; e += kThreads4) sm.hmask[e] = 0;
+  for (int e = tid; e < G * D / 4; e += kThreads4) sm.kept.w[e] = 0u;
   __syncthreads();
-  const size_t row0 = (size_t)b * hq + (size_t)g * G;
-  for (int e = tid; e < G * keep; e += kThreads4) {
-    const int h = e / keep;
-    const int ch = sel[(row0 + h) * keep + e % keep];
-    if (ch >= 0 && ch < D) {
-      atomicOr(&sm.hmask[ch], 1 << h);
-      sm.coefc[h][ch] = qp[(row0 + h) * D + ch] * scale2;
-    }
+#pragma unroll
+  for (int k = 0; k < SJ; ++k) {
+    const int e = tid + kThreads4 * k;
+    if (e < G * keep && sv[k] >= 0 && sv[k] < D) sm.kept.b[e / keep][sv[k]] = 1;
   }
   __syncthreads();
+#pragma unroll
+  for (int k = 0; k < SJ; ++k) {
+    // head h and half of element e are the same for the whole wavefront
+    const int e = tid + kThreads4 * k, h = e / D, ch = e % D;
+    const float cv = sm.kept.b[h][ch] ? qv[k] * scale2 : 0.0f;
+    sm.coefc[h][ch] = cv;
+    const float mx = wave_max(ch >= 1 ? fabsf(cv) : 0.0f);   // largest |coefficient| over channels >= 1
+    if (lane == 0) sm.redm[h][ch / 64] = mx;
+  }
   {
-    const bool f = tid < D && tid >= 1 && sm.hmask[tid] != 0;
+    const bool f = tid >= 1 && tid < D &&
+                   (sm.kept.b[0][tid % D] | sm.kept.b[1][tid % D] | sm.kept.b[2][tid % D] | sm.kept.b[3][tid % D]);
     const unsigned long long m = __ballot(f);
     if (lane == 0 && wave < 2) sm.wcount[wave] = __popcll(m);
-#pragma unroll
-    for (int h = 0; h < G; ++h) {   // largest |coefficient| of each head over channels >= 1
-      const float v = (tid >= 1 && tid < D) ? fabsf(sm.coefc[h][tid]) : 0.0f;
-      const float mx = wave_max(v);
-      if (lane == 0) sm.redm[h][wave] = mx;
-    }
     __syncthreads();
     if (f) sm.ulist[__popcll(m & ((1ull << lane) - 1ull)) + (wave == 1 ? sm.wcount[0] : 0)] = (int16_t)tid;
   }
@@ -305,28 +320,48 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
   const int nkc = (nu + 15) / 16;
   for (int e = tid; e < G * D; e += kThreads4) {
     const int h = e / D, i = e % D;
-    float mx = sm.redm[h][0];
-#pragma unroll
-    for (int w = 1; w < kWaves4; ++w) mx = fmaxf(mx, sm.redm[h][w]);
+    const float mx = D > 64 ? fmaxf(sm.redm[h][0], sm.redm[h][1]) : sm.redm[h][0];
     int ex = 0;
     if (mx > 0.0f) frexpf(mx, &ex);
     sm.coefs[h][i] = i < nu ? sm.coefc[h][sm.ulist[i]] * ldexpf(1.0f, -ex) : 0.0f;
     if (i == 0) sm.e2[h] = ldexpf(1.0f, ex);
   }
+  // Tokens of the unfinished last key group (only in the workgroup that reaches
+  // it): exact logits from the fp32 tail keys, one per (head, token).
+  if (t_body < t_end) {
+    if (tid < G * kGroup) {
+      const int h = tid / kGroup, r = tid % kGroup, t = t_body + r;
+      float zz = -INFINITY;
+      if (t < t_end) {
+        zz = sm.coefc[h][0] * f16_value(c0row[t]);
+        const float *row = tail + (size_t)r * D;
+        for (int i = 0; i < nu; ++i) {
+          const int ch = sm.ulist[i];
+          zz = fmaf(sm.coefc[h][ch], row[ch], zz);
+        }
+      }
+      sm.tailz[h][r] = zz;
+    }
+  }
   __syncthreads();
 
-  // ---------------------------------------------------------------- block loads (every lane)
   // Loads go through buffer resources of the unit's planes whose base is moved
-  // to the block (scalar arithmetic; the per-lane offsets stay fixed): an offset
-  // past the resource returns zero, so absent parts point past the end (kFar)
-  // and a block past the end gets an empty resource.
+  // to the block or tile (scalar arithmetic; the per-lane offsets stay fixed):
+  // an offset past the resource returns zero, so absent parts point past the
+  // end (kFar) and a block past the end gets an empty resource.
   const uint32_t kc_bytes = (uint32_t)(D * kc_stride), ks_bytes = (uint32_t)(D * ks_stride * 2);
   const uint32_t c0_bytes = (uint32_t)(c.capacity * 2), vw_bytes = (uint32_t)((c.capacity / 16) * D * 4);
   const uint32_t vs_bytes = (uint32_t)(c.capacity * L::VG * 2);
+  auto rsrc = [&](const void *base, uint32_t bytes, uint32_t off, bool live) {
+    // off < bytes for every live block or tile (its first token is below len <= capacity)
+    return __builtin_amdgcn_make_buffer_rsrc((void *)((const char *)base + (live ? off : 0u)), (short)0,
+                                             live ? (int)(bytes - off) : 0, kRsrcWord3);
+  };
 
+  // ---------------------------------------------------------------- key loads (every lane)
   // Every lane has one job of each kind, so that no write to LDS depends on the
-  // lane; at head_dim 64 the upper lanes repeat the key-code and value jobs of
-  // the lower ones (the same bytes to the same place).
+  // lane; at head_dim 64 the upper lanes repeat the key-code jobs of the lower
+  // ones (the same bytes to the same place).
   // key codes: slot octet lo, 16-token quarter lq of the block; 8 slots x 4 bytes
   const int lo = (tid >> 4) % L::OCT, lq = tid & 15;
   uint32_t kvo[8];
@@ -344,52 +379,29 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
     const int sl = j >> 2;
     ksv[k] = sl < nu ? (uint32_t)(sm.ulist[sl] * ks_stride * 2) + 4u * (j & 3) : kFar;
   }
-  // value words: 16-byte chunks tid, tid + 256 of the block's 16 rows of D words
-  int vch[2];
-  uint32_t vwo[2];
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    vch[k] = (tid + kThreads4 * k) % L::VCH;
-    vwo[k] = (uint32_t)((vch[k] / (D / 4)) * D * 4 + (vch[k] % (D / 4)) * 16);
-  }
-  // value scales (lanes below SCH) or channel 0 (the next 32 lanes): chunk tid of misc
-  constexpr int C0CH = kBlock4 * 2 / 16;
-  const uint32_t vso = tid < L::SCH ? 16u * tid : kFar;
-  const uint32_t c0o = (tid >= L::SCH && tid < L::SCH + C0CH) ? 16u * (tid - L::SCH) : kFar;
+  // channel 0: dword tid (tokens 2 tid, 2 tid + 1) for the lower 128 lanes
+  const uint32_t c0o = tid < kBlock4 / 2 ? 4u * tid : kFar;
 
-  // Every call issues the same loads, also for blocks past the end (they point
-  // past the planes): the count of loads in flight is then the same on every
-  // path, and the waits before a block's registers are used stay partial.
-  auto rsrc = [&](const void *base, uint32_t bytes, uint32_t off, bool live) {
-    // off < bytes for every live block (p0 < len <= capacity)
-    return __builtin_amdgcn_make_buffer_rsrc((void *)((const char *)base + (live ? off : 0u)), (short)0,
-                                             live ? (int)(bytes - off) : 0, kRsrcWord3);
-  };
-  auto issue = [&](Stage4<D> &S, int bk) {
+  // Every call issues the same loads, also for blocks past the end: the count of
+  // loads in flight is then the same on every path, and the waits before a
+  // block's registers are used stay partial.
+  auto kissue = [&](KStage4<D> &S, int p0, bool live) {
     __builtin_amdgcn_sched_barrier(0);
-    const bool live = bk < nb;
-    const uint32_t p0 = (uint32_t)(t_begin + kBlock4 * bk);
-    const auto rk = rsrc(kcodes, kc_bytes, p0 >> 2, live);
-    const auto rks = rsrc(kscales, ks_bytes, (p0 / kGroup) * 2u, live);
-    const auto rc0 = rsrc(c0row, c0_bytes, p0 * 2u, live);
-    const auto rvw = rsrc(vwords, vw_bytes, (p0 >> 4) * (uint32_t)(D * 4), live);
-    const auto rvs = rsrc(vscales, vs_bytes, p0 * (uint32_t)(L::VG * 2), live);
+    const uint32_t u0 = (uint32_t)p0;
+    const auto rk = rsrc(kcodes, kc_bytes, u0 >> 2, live);
+    const auto rks = rsrc(kscales, ks_bytes, (u0 / kGroup) * 2u, live);
+    const auto rc0 = rsrc(c0row, c0_bytes, u0 * 2u, live);
 #pragma unroll
     for (int cc = 0; cc < 8; ++cc) S.kc[cc] = __builtin_amdgcn_raw_buffer_load_b32(rk, kvo[cc], 0, 0);
 #pragma unroll
-    for (int k = 0; k < 2; ++k)
-      S.vw[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rvw, vwo[k], 0, 0));
-    S.vs = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rvs, vso, 0, 0));  // zero past the plane
-#pragma unroll
     for (int k = 0; k < KSD; ++k) S.ks[k] = __builtin_amdgcn_raw_buffer_load_b32(rks, ksv[k], 0, 0);
-    S.c0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc0, c0o, 0, 0));
+    S.c0 = __builtin_amdgcn_raw_buffer_load_b32(rc0, c0o, 0, 0);
     // keep the blocks' loads in issue order: a block's loads must all be older
-    // than the next block's for the partial waits above to apply
+    // than the next block's for the partial waits to apply
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  auto commit = [&](Stage4<D> &S, Block4<D> &B, int bk) {
-    const int p0 = t_begin + kBlock4 * bk;
+  auto kcommit = [&](KStage4<D> &S, KBlock4<D> &B, int p0) {
     {
       uint32_t y0[4], y1[4];
 #pragma unroll
@@ -410,20 +422,20 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
       dst[1] = u32x4{y0[2], y1[2], y0[3], y1[3]};
     }
     // key scales of a key group past the coded range (the exact tail or beyond) stay zero
+    const bool whole = p0 + kBlock4 <= code_end;   // workgroup-uniform
 #pragma unroll
     for (int k = 0; k < KSD; ++k) {
       const int j = tid + kThreads4 * k;
       const int sl = j >> 2, gp = 2 * (j & 3);
-      const int g0 = p0 / kGroup + gp;
-      const uint32_t v = S.ks[k];
-      B.ksig[gp][sl] = g0 * kGroup < code_end ? (uint16_t)v : (uint16_t)0;
-      B.ksig[gp + 1][sl] = (g0 + 1) * kGroup < code_end ? (uint16_t)(v >> 16) : (uint16_t)0;
+      uint32_t v = S.ks[k];
+      if (!whole) {
+        const int g0 = p0 / kGroup + gp;
+        v &= (g0 * kGroup < code_end ? 0xffffu : 0u) | ((g0 + 1) * kGroup < code_end ? 0xffff0000u : 0u);
+      }
+      B.ksig[gp][sl] = (uint16_t)v;
+      B.ksig[gp + 1][sl] = (uint16_t)(v >> 16);
     }
-#pragma unroll
-    for (int k = 0; k < 2; ++k)
-      *reinterpret_cast<u32x4 *>(&B.vw[vch[k] / (D / 4)][(vch[k] % (D / 4)) * 4]) = S.vw[k];
-    // at most one of the two is not zero (the other load pointed past its plane)
-    B.misc.chunk[tid] = S.vs | S.c0;
+    B.c0w[tid] = S.c0;
   };
 
   // ---------------------------------------------------------------- per-wavefront state
@@ -455,41 +467,12 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) ez[hh][nt] = ldexpf(e, 25 - 2 * (3 + nt));
   }
-  // value A producer: my tokens are c = 2(n&7), c+1 of word 2lg + (n>>3)
-  const int pw = 2 * lg + (n >> 3), pkc = (n >> 1) & 1, pi0 = 4 * (n & 1) + ((n >> 2) & 1);
-  const int pk[2] = {value_k(2 * (n & 3)), value_k(2 * (n & 3) + 1)};
-
-  // running state
-  float m_run[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) m_run[h] = 0.0f;
-  float mr[2] = {0.0f, 0.0f};
-  int f_run = 0, es_run = -24;
-  uint32_t sbound = 0x7C00u;
-  float fp[2], thr[2];
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    fp[nt] = (float)(f_run + 24 - 2 * pk[nt]);
-    thr[nt] = kSlack + fp[nt];
-  }
-  bool first = true;
-  float lacc[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
-  f32x4 vacc[L::VG][2], sacc[L::VG];
-#pragma unroll
-  for (int j = 0; j < L::VG; ++j) {
-    vacc[j][0] = vacc[j][1] = sacc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  }
   u32x4 alog[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};   // logit A operands: zero in off-diagonal lanes
-  u32x4 aval[2];   // value A operands
   u32x4 ones = {kOneF16x2, kOneF16x2, kOneF16x2, kOneF16x2};
-  const u32x4 unit_k[2] = {{0x00010001u, 0x00040004u, 0x00100010u, 0x00400040u},
-                           {0x01000100u, 0x00100010u, 0x00400040u, 0x01000100u}};
 
-  // ---------------------------------------------------------------- one tile of one block
-  auto compute = [&](const Block4<D> &B, int bk) {
-    const int tile0 = t_begin + kBlock4 * bk + kTile4 * wave;
-    if (tile0 >= t_end) return;
-
+  // Logits (log2 units) of this wavefront's tile of one block: z[hh][nt] for head
+  // 2hp + hh and token tile0 + 32lg + 2n + nt; -inf past the end of the split.
+  auto logits = [&](const KBlock4<D> &B, int tile0, float (&z)[2][2]) {
     // ---- logit A operands of the tile's two key groups (compact build)
     {
       const u32x4 *src = reinterpret_cast<const u32x4 *>(&B.ksig[2 * wave + ab_g][ab_s]);
@@ -524,155 +507,153 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
     }
     wave_sync();
 
-    // ---- logits: C rows (group lg, heads 2hp, 2hp+1, high/low), columns tokens 32lg + 2n + nt
+    // ---- C rows (group lg, heads 2hp, 2hp+1, high/low), columns tokens 32lg + 2n + nt
     f32x4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = acc0, accs = acc0;
     asm volatile("" : "+v"(ones));
     {
-      u32x2 dd[2];
-      if (nkc > 0) {
-        if (arow) alog[0] = *reinterpret_cast<const u32x4 *>(&W.u.t.abuf[n][8 * (q & 1)]);
-        dd[0] = *reinterpret_cast<const u32x2 *>(&B.y[wave][q & 1][8 * lg + (n >> 1)][0]);
-      }
+      // every K chunk is worked on (slots past |U| have zero codes and zero
+      // coefficients): straight-line code without branches between the products
+      const uint16_t *arow_base = arow ? &W.u.t.abuf[n][8 * (q & 1)] : reinterpret_cast<const uint16_t *>(&W.zero);
+      const int astep = arow ? 16 : 0;
 #pragma unroll
       for (int kc = 0; kc < L::NKC; ++kc) {
-        if (kc < nkc) {
-          const int cur = kc & 1, nxt = cur ^ 1;
-          if (kc + 1 < L::NKC && kc + 1 < nkc) {
-            if (arow) alog[nxt] = *reinterpret_cast<const u32x4 *>(&W.u.t.abuf[n][16 * (kc + 1) + 8 * (q & 1)]);
-            dd[nxt] = *reinterpret_cast<const u32x2 *>(&B.y[wave][2 * (kc + 1) + (q & 1)][8 * lg + (n >> 1)][0]);
-          }
-          const uint32_t l0 = pk_shl16(dd[cur].x, shl2), h0 = pk_shr16(dd[cur].x, shr2);
-          const uint32_t l1 = pk_shl16(dd[cur].y, shl2), h1 = pk_shr16(dd[cur].y, shr2);
-          constexpr uint32_t M3 = 0x00C000C0u, M4 = 0x03000300u;
-          const u32x4 b0 = {l0 & M3, h0 & M3, l1 & M3, h1 & M3};   // token r0: u 2^-18
-          const u32x4 b1 = {l0 & M4, h0 & M4, l1 & M4, h1 & M4};   // token r0+1: u 2^-16
-          acc0 = mfma16(alog[cur], b0, acc0);
-          acc1 = mfma16(alog[cur], b1, acc1);
-          accs = mfma16(alog[cur], ones, accs);
-        }
+        const u32x4 al = *reinterpret_cast<const u32x4 *>(arow_base + astep * kc);
+        const u32x2 dk = *reinterpret_cast<const u32x2 *>(&B.y[wave][2 * kc + (q & 1)][8 * lg + (n >> 1)][0]);
+        const uint32_t l0 = pk_shl16(dk.x, shl2), h0 = pk_shr16(dk.x, shr2);
+        const uint32_t l1 = pk_shl16(dk.y, shl2), h1 = pk_shr16(dk.y, shr2);
+        constexpr uint32_t M3 = 0x00C000C0u, M4 = 0x03000300u;
+        const u32x4 b0 = {l0 & M3, h0 & M3, l1 & M3, h1 & M3};   // token r0: u 2^-18
+        const u32x4 b1 = {l0 & M4, h0 & M4, l1 & M4, h1 & M4};   // token r0+1: u 2^-16
+        acc0 = mfma16(al, b0, acc0);
+        acc1 = mfma16(al, b1, acc1);
+        accs = mfma16(al, ones, accs);
       }
     }
-
-    // ---- this tile's channel 0, value scales and value words from the block
     const int tt = kTile4 * wave + 32 * lg + 2 * n;   // my first token within the block
-    const uint32_t cx0 = *reinterpret_cast<const uint32_t *>(&B.misc.m.c0[tt]);
-    uint32_t cvs[L::VG];
-    {
-      // value scales of tokens past the split end are zero (their numerators are zero too)
-      const int t0 = tile0 + 32 * lg + 2 * n;
-      const uint32_t m0 = t0 < t_end ? 0xffffffffu : 0u, m1 = t0 + 1 < t_end ? 0xffffffffu : 0u;
-      if constexpr (L::VG == 4) {
-        const u32x4 x = *reinterpret_cast<const u32x4 *>(&B.misc.m.vs[tt][0]);
-        cvs[0] = x.x & m0; cvs[1] = x.y & m0; cvs[2] = x.z & m1; cvs[3] = x.w & m1;
-      } else {
-        const u32x2 x = *reinterpret_cast<const u32x2 *>(&B.misc.m.vs[tt][0]);
-        cvs[0] = x.x & m0; cvs[1] = x.y & m1;
-      }
-    }
-
-    // ---- logits (log2 units) relative to the running max, plus the value exponent
-    float zp[2][2];
+    const uint32_t cx0 = B.c0w[tt >> 1];
     const float x0f[2] = {h2f(cx0 & 0xffffu), h2f(cx0 >> 16)};
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       const float cs = accs[2 * hh] + accs[2 * hh + 1];
-      const float bb = fmaf(n3e[hh], cs, -mr[hh]);
+      const float bb = n3e[hh] * cs;
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         const f32x4 &a = nt == 0 ? acc0 : acc1;
         const float u = a[2 * hh] + a[2 * hh + 1];
-        const float w = fmaf(c0c[hh], x0f[nt], bb + fp[nt]);
-        zp[hh][nt] = fmaf(ez[hh][nt], u, w);
+        z[hh][nt] = fmaf(ez[hh][nt], u, fmaf(c0c[hh], x0f[nt], bb));
       }
     }
     const int tl0 = tile0 + 32 * lg + 2 * n;   // my first token
     if (tile0 + kTile4 > t_end) {
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
-        if (tl0 + nt >= t_end) zp[0][nt] = zp[1][nt] = -INFINITY;
+        if (tl0 + nt >= t_end) z[0][nt] = z[1][nt] = -INFINITY;
     }
-    // tokens of the unfinished last group: exact fp32 tail keys
+    // tokens of the unfinished last group: the exact logits computed up front
     if (tile0 + kTile4 > t_body && t_body < t_end) {
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         const int t = tl0 + nt;
         if (t >= t_body && t < t_end) {
-          const float *row = tail + (size_t)(t & 31) * D;
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const int h = 2 * hp + hh;
-            float zz = sm.coefc[h][0] * x0f[nt];
-            for (int i = 0; i < nu; ++i) {
-              const int ch = sm.ulist[i];
-              zz = fmaf(sm.coefc[h][ch], row[ch], zz);
-            }
-            zp[hh][nt] = zz - mr[hh] + fp[nt];
-          }
+          z[0][nt] = sm.tailz[2 * hp][t - t_body];
+          z[1][nt] = sm.tailz[2 * hp + 1][t - t_body];
         }
       }
     }
+  };
 
-    // ---- running maximum / value exponent: move only when needed (wavefront-uniform)
+  // ---------------------------------------------------------------- value loads (per wavefront)
+  // value A producer: my tokens are c = 2(n&7), c+1 of word 2lg + (n>>3)
+  const int pw = 2 * lg + (n >> 3), pkc = (n >> 1) & 1, pi0 = 4 * (n & 1) + ((n >> 2) & 1);
+  const int pk[2] = {value_k(2 * (n & 3)), value_k(2 * (n & 3) + 1)};
+  const uint32_t vwv = (uint32_t)(16 * q + n) * 4u;                   // word row 0, channel 16q + n of the tile
+  const uint32_t vsv = (uint32_t)(32 * lg + 2 * n) * (uint32_t)(L::VG * 2);   // scales of my two tokens
+
+  auto vissue = [&](VStage4<D> &V, int tile0, bool live) {
+    __builtin_amdgcn_sched_barrier(0);
+    live = live && tile0 < t_end;
+    const uint32_t u0 = (uint32_t)tile0;
+    const auto rvw = rsrc(vwords, vw_bytes, (u0 >> 4) * (uint32_t)(D * 4), live);
+    const auto rvs = rsrc(vscales, vs_bytes, u0 * (uint32_t)(L::VG * 2), live);
+#pragma unroll
+    for (int hf = 0; hf < L::NH; ++hf)
+#pragma unroll
+      for (int wr = 0; wr < 4; ++wr)
+        V.vw[hf][wr] = __builtin_amdgcn_raw_buffer_load_b32(rvw, vwv + (uint32_t)(wr * D + 64 * hf) * 4u, 0, 0);
+    if constexpr (L::VG == 4) {
+      const u32x4 x = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rvs, vsv, 0, 0));
+      V.vs[0] = x.x; V.vs[1] = x.y; V.vs[2] = x.z; V.vs[3] = x.w;
+    } else {
+      const u32x2 x = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rvs, vsv, 0, 0));
+      V.vs[0] = x.x; V.vs[1] = x.y;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // ---------------------------------------------------------------- running state
+  float m_run[G];      // per head: the maximum logit so far (-inf before any)
+#pragma unroll
+  for (int h = 0; h < G; ++h) m_run[h] = -INFINITY;
+  int f_run = 0, es_run = -24;
+  uint32_t sbound = 0u;   // fp16 bits of 2^es_run: a larger value scale moves F
+  bool firstv = true;
+  float fp[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) fp[nt] = (float)(f_run + 24 - 2 * pk[nt]);
+  float lacc[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
+  // Weighted sum: one product per 8 tokens and 64 channels, block diagonal in K:
+  // C[4jj + h][n] = sum over the 8 tokens of A[h][t] B[t][16jj + n], K = (jj, t),
+  // so lane (n, q) accumulates heads 0-3 of channel 64 half + 16q + n.
+  f32x4 vacc[L::NH];
+#pragma unroll
+  for (int hf = 0; hf < L::NH; ++hf) vacc[hf] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  // S = 2^F sum p scale per (head 2hp + hh, value group j), from the same fp16
+  // operands (each scaled back by the 2^(2k-24) of its token), partial per lane.
+  float sacc[2][L::VG];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+    for (int j = 0; j < L::VG; ++j) sacc[hh][j] = 0.0f;
+  const float kback[2] = {ldexpf(1.0f, 2 * pk[0] - 24), ldexpf(1.0f, 2 * pk[1] - 24)};
+  if (lane == 0) W.zero = u32x4{0u, 0u, 0u, 0u};
+
+  // One tile of values: numerators from the stored logits, weighted sum of the codes.
+  auto values = [&](const VStage4<D> &V, int tile0, const float (&z)[2][2], const float (&mr)[2]) {
+    // value scales of tokens past the split end are zero (their numerators are zero too)
+    const int t0 = tile0 + 32 * lg + 2 * n;
+    const uint32_t m0 = t0 < t_end ? 0xffffffffu : 0u, m1 = t0 + 1 < t_end ? 0xffffffffu : 0u;
+    uint32_t cvs[L::VG];
+#pragma unroll
+    for (int i = 0; i < L::VG; ++i) cvs[i] = V.vs[i] & (i < L::VG / 2 ? m0 : m1);
+
+    // ---- value exponent F: moves only when a value scale outgrows 2^es_run
     uint32_t smax = 0;
 #pragma unroll
     for (int i = 0; i < L::VG; ++i) smax = max(smax, max(cvs[i] & 0xffffu, cvs[i] >> 16));
-    const bool over = zp[0][0] > thr[0] || zp[1][0] > thr[0] || zp[0][1] > thr[1] ||
-                      zp[1][1] > thr[1] || smax >= sbound;
-    if (first || __ballot(over) != 0ull) {
-      float d[G];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        float zm = fmaxf(zp[hh][0] - fp[0], zp[hh][1] - fp[1]);
-        zm = row16_max(zm);
-        const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, zm), 0));
-        const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, zm), 16));
-        const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, zm), 32));
-        const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, zm), 48));
-        d[hh] = fmaxf(r0, r2);        // head hh   (rows q = 0, 2)
-        d[2 + hh] = fmaxf(r1, r3);    // head 2+hh (rows q = 1, 3)
-      }
+    if (firstv || __ballot(smax >= sbound) != 0ull) {
       const float sv = wave_max(h2f(smax));
       int es_t = -24;
       if (sv > 0.0f) frexpf(sv, &es_t);
-      const int es_new = first ? es_t : max(es_run, es_t);
-      const int f_new = 15 - (int)kSlack - 24 - es_new;
-      const float beta = first ? 1.0f : ldexpf(1.0f, f_new - f_run);
-      float al[G], dm[G];
+      const int es_new = firstv ? es_t : max(es_run, es_t);
+      const int f_new = 15 - 24 - es_new;
+      if (!firstv) {
+        const float beta = ldexpf(1.0f, f_new - f_run);
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        dm[h] = first ? d[h] : fmaxf(d[h], 0.0f);
-        m_run[h] += dm[h];
-        al[h] = first ? 1.0f : exp2f(-dm[h]) * beta;
-      }
+        for (int hf = 0; hf < L::NH; ++hf) vacc[hf] *= beta;
 #pragma unroll
-      for (int j = 0; j < L::VG; ++j)
+        for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          vacc[j][0][i] *= al[i];
-          vacc[j][1][i] *= al[i];
-          sacc[j][i] *= al[i];
-        }
-      const float df = (float)(f_new - f_run);
+          for (int j = 0; j < L::VG; ++j) sacc[hh][j] *= beta;
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const float a = sel2(hp, al[hh], al[2 + hh]);
-        const float dmh = sel2(hp, dm[hh], dm[2 + hh]);
-        mr[hh] = sel2(hp, m_run[hh], m_run[2 + hh]);
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          lacc[hh][nt] *= a;
-          zp[hh][nt] += df - dmh;
+          for (int nt = 0; nt < 2; ++nt) lacc[hh][nt] *= beta;
         }
       }
       f_run = f_new;
       es_run = es_new;
       sbound = pow2_bits(es_new);
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        fp[nt] = (float)(f_run + 24 - 2 * pk[nt]);
-        thr[nt] = kSlack + fp[nt];
-      }
-      first = false;
+      for (int nt = 0; nt < 2; ++nt) fp[nt] = (float)(f_run + 24 - 2 * pk[nt]);
+      firstv = false;
     }
 
     // ---- numerators -> value A operands (row = head, K = token)
@@ -681,7 +662,7 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        p[hh][nt] = __builtin_amdgcn_exp2f(zp[hh][nt]);
+        p[hh][nt] = __builtin_amdgcn_exp2f(z[hh][nt] - mr[hh] + fp[nt]);
         lacc[hh][nt] += p[hh][nt];
       }
 #pragma unroll
@@ -691,65 +672,132 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         uint16_t *dst = &W.u.t.pbuf[j][pkc][2 * hp + hh][pw][pi0];
-        if (j & 1) {
-          dst[0] = (uint16_t)mixlo<1>(p[hh][0], s0);
-          dst[2] = (uint16_t)mixlo<1>(p[hh][1], s1);
-        } else {
-          dst[0] = (uint16_t)mixlo<0>(p[hh][0], s0);
-          dst[2] = (uint16_t)mixlo<0>(p[hh][1], s1);
-        }
+        const uint32_t a0 = (j & 1) ? mixlo<1>(p[hh][0], s0) : mixlo<0>(p[hh][0], s0);
+        const uint32_t a1 = (j & 1) ? mixlo<1>(p[hh][1], s1) : mixlo<0>(p[hh][1], s1);
+        dst[0] = (uint16_t)a0;
+        dst[2] = (uint16_t)a1;
+        sacc[hh][j] = mix_acc(sacc[hh][j], a0, kback[0]);
+        sacc[hh][j] = mix_acc(sacc[hh][j], a1, kback[1]);
       }
     }
     wave_sync();
 
-    // ---- weighted sum of the value codes
-    // rows 4..15 of the value A operand are never read: every lane loads (head n mod 4)
-    u32x2 cvw[L::VG];
+    // ---- weighted sum of the value codes: A of lane (row 4jj + h, K group q) is
+    // head h's 8 numerators of value group 2 half + jj/2 when q == jj, else zero
+    const int jj = n >> 2, ah = n & 3;
 #pragma unroll
-    for (int j = 0; j < L::VG; ++j)
-      cvw[j] = *reinterpret_cast<const u32x2 *>(&B.vw[4 * wave + q][32 * j + 2 * n]);
-    aval[0] = *reinterpret_cast<const u32x4 *>(&W.u.t.pbuf[0][0][n & 3][q][0]);
+    for (int hf = 0; hf < L::NH; ++hf)
 #pragma unroll
-    for (int kc2 = 0; kc2 < 2; ++kc2) {
+      for (int wr = 0; wr < 4; ++wr)
 #pragma unroll
-      for (int j = 0; j < L::VG; ++j) {
-        const int step = kc2 * L::VG + j, cur = step & 1;
-        if (step + 1 < 2 * L::VG) {
-          const int j2 = (step + 1) % L::VG, k2 = (step + 1) / L::VG;
-          aval[cur ^ 1] = *reinterpret_cast<const u32x4 *>(&W.u.t.pbuf[j2][k2][n & 3][q][0]);
+        for (int kc2 = 0; kc2 < 2; ++kc2) {
+          const u32x4 *src = q == jj ? reinterpret_cast<const u32x4 *>(&W.u.t.pbuf[2 * hf + (jj >> 1)][kc2][ah][wr][0])
+                                     : &W.zero;
+          vacc[hf] = mfma16(*src, value_operand(V.vw[hf][wr], kc2), vacc[hf]);
         }
-        sacc[j] = mfma16(aval[cur], unit_k[kc2], sacc[j]);
-        vacc[j][0] = mfma16(aval[cur], value_operand(cvw[j].x, kc2), vacc[j][0]);
-        vacc[j][1] = mfma16(aval[cur], value_operand(cvw[j].y, kc2), vacc[j][1]);
-      }
-    }
     wave_sync();
   };
 
-  // ---------------------------------------------------------------- block pipeline
-  // Two blocks in flight in registers; block bk is written to LDS buffer bk & 1
-  // once its loads have landed, published by one barrier, then computed.  The
-  // barrier of block bk also tells every wavefront that block bk - 1, which
-  // used the other buffer, has been computed by all of them.
-  // Blocks go in pairs; a block past the end is all zeros and computes nothing.
-  Stage4<D> S0, S1;
-  issue(S0, 0);
-  issue(S1, 1);
-  for (int bk = 0; bk < nb; bk += 2) {
-    commit(S0, sm.blk[0], bk);
-    issue(S0, bk + 2);
-    block_barrier();
-    compute(sm.blk[0], bk);
-    commit(S1, sm.blk[1], bk + 1);
-    issue(S1, bk + 3);
-    block_barrier();
-    compute(sm.blk[1], bk + 1);
+  // ---------------------------------------------------------------- chunks
+  for (int cb = 0; cb < nb; cb += kChunk4) {
+    // a wavefront that is through with the previous chunk waits here until the
+    // others have also read the key blocks of its last two blocks
+    if (cb > 0) block_barrier();
+    const int nbc = min(kChunk4, nb - cb);           // blocks in this chunk
+    const int c_t0 = t_begin + kBlock4 * cb;         // first token of the chunk
+    float zs[kChunk4][2][2];                         // this wavefront's logits of the chunk
+    float zl[2] = {-INFINITY, -INFINITY};            // and their maximum per head of the pair
+
+    // ---- pass 1: keys.  Four blocks are in flight in registers.  Block i is
+    // written to LDS buffer i & 1 once its loads have landed, published by one
+    // barrier, then worked on; the barrier of block i also tells every
+    // wavefront that block i - 1, which used the other buffer, has been worked
+    // on by all of them.
+    KStage4<D> S0, S1;
+    kissue(S0, c_t0, 0 < nbc);
+    kissue(S1, c_t0 + kBlock4, 1 < nbc);
+#pragma unroll
+    for (int i = 0; i < kChunk4; ++i) {
+      if (i >= nbc) break;
+      KStage4<D> &S = (i & 1) ? S1 : S0;
+      const int p0 = c_t0 + kBlock4 * i;
+      kcommit(S, sm.kb[i & 1], p0);
+      kissue(S, p0 + 2 * kBlock4, i + 2 < nbc);
+      block_barrier();
+      const int tile0 = p0 + kTile4 * wave;
+      if (tile0 < t_end) {
+        logits(sm.kb[i & 1], tile0, zs[i]);
+      } else {
+        zs[i][0][0] = zs[i][0][1] = zs[i][1][0] = zs[i][1][1] = -INFINITY;
+      }
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) zl[hh] = fmaxf(zl[hh], fmaxf(zs[i][hh][0], zs[i][hh][1]));
+    }
+
+    // ---- pass 2: values; the first three tiles are on their way during the maximum
+    VStage4<D> V0, V1, V2;
+    vissue(V0, c_t0 + kTile4 * wave, true);
+    vissue(V1, c_t0 + kBlock4 + kTile4 * wave, 1 < nbc);
+    vissue(V2, c_t0 + 2 * kBlock4 + kTile4 * wave, 2 < nbc);
+
+    // exact maximum of each head's logits in the chunk (wavefront-uniform)
+    float d[G];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const float zm = row16_max(zl[hh]);
+      const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, zm), 0));
+      const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, zm), 16));
+      const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, zm), 32));
+      const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, zm), 48));
+      d[hh] = fmaxf(r0, r2);        // head hh   (rows q = 0, 2)
+      d[2 + hh] = fmaxf(r1, r3);    // head 2+hh (rows q = 1, 3)
+    }
+    // a head whose maximum rises rescales what was accumulated before this chunk
+    bool rise = false;
+    float al[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float mn = fmaxf(m_run[h], d[h]);
+      al[h] = (m_run[h] == -INFINITY || mn == m_run[h]) ? 1.0f : exp2f(m_run[h] - mn);
+      rise = rise || (m_run[h] != -INFINITY && mn > m_run[h]);
+      m_run[h] = mn;
+    }
+    if (rise) {
+#pragma unroll
+      for (int hf = 0; hf < L::NH; ++hf)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vacc[hf][i] *= al[i];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const float a = sel2(hp, al[hh], al[2 + hh]);
+#pragma unroll
+        for (int j = 0; j < L::VG; ++j) sacc[hh][j] *= a;
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) lacc[hh][nt] *= a;
+      }
+    }
+    // subtracted from my heads' logits (0 for a head with no logit yet: its numerators are 0)
+    float mr[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const float m = sel2(hp, m_run[hh], m_run[2 + hh]);
+      mr[hh] = m == -INFINITY ? 0.0f : m;
+    }
+
+#pragma unroll
+    for (int i = 0; i < kChunk4; ++i) {
+      if (i >= nbc) break;
+      VStage4<D> &V = (i % 3 == 0) ? V0 : (i % 3 == 1) ? V1 : V2;
+      const int tile0 = c_t0 + kBlock4 * i + kTile4 * wave;
+      if (tile0 < t_end) values(V, tile0, zs[i], mr);
+      vissue(V, tile0 + 3 * kBlock4, i + 3 < nbc);
+    }
   }
-  // the loads of the two blocks past the end (they return zeros) land before the merge
+  // loads of tiles past the end (they return zeros) land before the merge
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---------------------------------------------------------------- merge the wavefronts
-  const bool had = t_begin + kTile4 * wave < t_end;   // this wavefront computed a tile
+  const bool had = t_begin + kTile4 * wave < t_end;   // this wavefront had tokens
   {
     float lh[G];
 #pragma unroll
@@ -763,15 +811,31 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
       lh[hh] = r0 + r2;
       lh[2 + hh] = r1 + r3;
     }
+    // S per (head, value group): sum over the 32 lanes of each head pair
+    float sh[G][L::VG];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int j = 0; j < L::VG; ++j) {
+        const float v = row16_sum(sacc[hh][j]);
+        const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+        const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+        const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+        const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+        sh[hh][j] = r0 + r2;
+        sh[2 + hh][j] = r1 + r3;
+      }
     const float inv_f = ldexpf(1.0f, -f_run);
-    if (q == 0) {
 #pragma unroll
-      for (int j = 0; j < L::VG; ++j)
+    for (int hf = 0; hf < L::NH; ++hf) {
+      const int ch = 64 * hf + 16 * q + n;
+      const int j = ch / 32;   // 2 hf + (q >> 1)
 #pragma unroll
-        for (int e = 0; e < 2; ++e)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            W.u.merge[i][32 * j + 2 * n + e] = (2.0f * vacc[j][e][i] - 3.0f * sacc[j][i]) * inv_f;
+      for (int i = 0; i < 4; ++i) {
+        const float si = (q >> 1) ? sh[i][2 * hf + 1] : sh[i][2 * hf];
+        W.u.merge[i][ch] = (2.0f * vacc[hf][i] - 3.0f * si) * inv_f;
+      }
+      (void)j;
     }
 #pragma unroll
     for (int h = 0; h < G; ++h)
