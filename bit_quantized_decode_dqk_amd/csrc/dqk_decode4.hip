@@ -73,9 +73,8 @@ struct Lay4 {
   static constexpr int OCT = D / 8;     // union-slot octets
   static constexpr int NKC = D / 16;    // logit K chunks (16 slots of each key group)
   static constexpr int VG = D / 32;     // value scale groups
-  static constexpr int SPL = D / 8;     // union slots per lane in the logit A build
   static constexpr int AROW = D + 8;    // fp16 per logit A row (padded against bank conflicts)
-  static constexpr int KSD = D / 64;    // key-scale dwords per lane per block (4 per slot)
+  static constexpr int SPJ = D / 2;     // logit A jobs (union-slot pair, key-group pair) per block / 4
   static constexpr int NH = D / 64;     // 64-channel halves of the weighted sum
 };
 
@@ -83,7 +82,9 @@ struct Lay4 {
 template <int D>
 struct __attribute__((aligned(16))) KBlock4 {
   uint32_t y[kWaves4][Lay4<D>::OCT][16][2];   // key codes: tile, slot octet, token quad, slots 0-3 | 4-7
-  uint16_t ksig[kKsPerBlock][D];              // key scales (fp16 bits): key group of the block, slot
+  // logit A operands of tile w: rows 8g + 2h + limb (key group g of the tile,
+  // head h, fp16 high/low part), slots in octet order 0,2,1,3,4,6,5,7
+  uint16_t a[kWaves4][16][Lay4<D>::AROW];
   uint32_t c0w[kThreads4];                    // key channel 0: fp16 pair of tokens 2i, 2i+1 (i < 128)
 };
 
@@ -92,7 +93,6 @@ struct __attribute__((aligned(16))) WaveSmem4 {
   u32x4 zero;   // a 16-byte zero operand
   union {
     struct {
-      uint16_t abuf[16][Lay4<D>::AROW];           // logit A rows 8g+2h+limb, slots in octet order 0,2,1,3,4,6,5,7
       uint16_t pbuf[Lay4<D>::VG][2][kG4][4][8];   // value A: group j, K chunk, head, word, K position
     } t;
     float merge[kG4][D];                          // the wavefront's output at the end of the split
@@ -121,7 +121,7 @@ struct __attribute__((aligned(16))) Smem4 {
 template <int D>
 struct KStage4 {
   uint32_t kc[8];              // key codes: 8 slots x 16 tokens
-  uint32_t ks[Lay4<D>::KSD];   // key scales: dwords (two groups of one slot each)
+  uint32_t ks[2];              // key scales of two slots: dwords (two groups each)
   uint32_t c0;                 // channel 0: two tokens
 };
 
@@ -370,14 +370,21 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
     const int i = 8 * lo + cc;
     kvo[cc] = i < nu ? (uint32_t)(sm.ulist[i] * kc_stride) + 4u * lq : kFar;
   }
-  // key scales: dword jobs j = tid (+ 256): slot j / 4, groups 2(j % 4), +1 of the block
-  constexpr int KSD = L::KSD;
-  uint32_t ksv[KSD];
+  // logit A operands, built here from the key scales: job j (one per lane; the
+  // upper lanes repeat the lower ones at head_dim 64) is key-group pair gp = tile
+  // j % 4 of the block and union slots s0 = 8o + a, s1 = s0 + 2 (a = 0, 1, 4, 5),
+  // which sit side by side in the octet order of the A rows
+  const int aj = tid % (4 * L::SPJ), agp = aj & 3, asp = aj >> 2;
+  const int aoct = asp >> 2, am = asp & 3;
+  const int as0 = 8 * aoct + (am & 1) + 4 * (am >> 1), as1 = as0 + 2;
+  uint32_t ksv[2];
+  ksv[0] = as0 < nu ? (uint32_t)(sm.ulist[as0] * ks_stride * 2) + 4u * agp : kFar;
+  ksv[1] = as1 < nu ? (uint32_t)(sm.ulist[as1] * ks_stride * 2) + 4u * agp : kFar;
+  float ca[G], cb[G];   // coefficients of the two slots per head (0 past |U|)
 #pragma unroll
-  for (int k = 0; k < KSD; ++k) {
-    const int j = tid + kThreads4 * k;
-    const int sl = j >> 2;
-    ksv[k] = sl < nu ? (uint32_t)(sm.ulist[sl] * ks_stride * 2) + 4u * (j & 3) : kFar;
+  for (int h = 0; h < G; ++h) {
+    ca[h] = sm.coefs[h][as0];
+    cb[h] = sm.coefs[h][as1];
   }
   // channel 0: dword tid (tokens 2 tid, 2 tid + 1) for the lower 128 lanes
   const uint32_t c0o = tid < kBlock4 / 2 ? 4u * tid : kFar;
@@ -394,7 +401,7 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
 #pragma unroll
     for (int cc = 0; cc < 8; ++cc) S.kc[cc] = __builtin_amdgcn_raw_buffer_load_b32(rk, kvo[cc], 0, 0);
 #pragma unroll
-    for (int k = 0; k < KSD; ++k) S.ks[k] = __builtin_amdgcn_raw_buffer_load_b32(rks, ksv[k], 0, 0);
+    for (int k = 0; k < 2; ++k) S.ks[k] = __builtin_amdgcn_raw_buffer_load_b32(rks, ksv[k], 0, 0);
     S.c0 = __builtin_amdgcn_raw_buffer_load_b32(rc0, c0o, 0, 0);
     // keep the blocks' loads in issue order: a block's loads must all be older
     // than the next block's for the partial waits to apply
@@ -421,19 +428,27 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
       dst[0] = u32x4{y0[0], y1[0], y0[1], y1[1]};
       dst[1] = u32x4{y0[2], y1[2], y0[3], y1[3]};
     }
-    // key scales of a key group past the coded range (the exact tail or beyond) stay zero
-    const bool whole = p0 + kBlock4 <= code_end;   // workgroup-uniform
+    // logit A operands: key scales of a key group past the coded range (the exact
+    // tail or beyond) count as zero.  High part = fp16 of the product, low part =
+    // fp16 of what the high part leaves out (about 22 significant bits together).
+    uint32_t v0 = S.ks[0], v1 = S.ks[1];
+    if (p0 + kBlock4 > code_end) {   // workgroup-uniform
+      const int g0 = p0 / kGroup + 2 * agp;
+      const uint32_t km = (g0 * kGroup < code_end ? 0xffffu : 0u) | ((g0 + 1) * kGroup < code_end ? 0xffff0000u : 0u);
+      v0 &= km;
+      v1 &= km;
+    }
 #pragma unroll
-    for (int k = 0; k < KSD; ++k) {
-      const int j = tid + kThreads4 * k;
-      const int sl = j >> 2, gp = 2 * (j & 3);
-      uint32_t v = S.ks[k];
-      if (!whole) {
-        const int g0 = p0 / kGroup + gp;
-        v &= (g0 * kGroup < code_end ? 0xffffu : 0u) | ((g0 + 1) * kGroup < code_end ? 0xffff0000u : 0u);
-      }
-      B.ksig[gp][sl] = (uint16_t)v;
-      B.ksig[gp + 1][sl] = (uint16_t)(v >> 16);
+    for (int h = 0; h < G; ++h) {
+      uint32_t hi0 = mixhi<0>(mixlo<0>(ca[h], v0), cb[h], v1);
+      uint32_t lo0 = reshi<0, 1>(reslo<0, 0>(ca[h], v0, hi0), cb[h], v1, hi0);
+      uint32_t hi1 = mixhi<1>(mixlo<1>(ca[h], v0), cb[h], v1);
+      uint32_t lo1 = reshi<1, 1>(reslo<1, 0>(ca[h], v0, hi1), cb[h], v1, hi1);
+      uint16_t (*ar)[L::AROW] = B.a[agp];
+      *reinterpret_cast<uint32_t *>(&ar[2 * h][8 * aoct + 2 * am]) = hi0;
+      *reinterpret_cast<uint32_t *>(&ar[2 * h + 1][8 * aoct + 2 * am]) = lo0;
+      *reinterpret_cast<uint32_t *>(&ar[8 + 2 * h][8 * aoct + 2 * am]) = hi1;
+      *reinterpret_cast<uint32_t *>(&ar[8 + 2 * h + 1][8 * aoct + 2 * am]) = lo1;
     }
     B.c0w[tid] = S.c0;
   };
@@ -443,11 +458,6 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
   const int q = lane >> 4, n = lane & 15;
   const int lg = q >> 1, hp = q & 1;   // logit lanes: key group of the tile, head pair (2hp, 2hp+1)
 
-  // logit A build: (group ab_g, head ab_h, slots ab_s .. ab_s+SPL-1)
-  const int ab_g = lane >> 5, ab_h = (lane >> 3) & 3, ab_s = L::SPL * (lane & 7);
-  float cf[L::SPL];
-#pragma unroll
-  for (int i = 0; i < L::SPL; ++i) cf[i] = sm.coefs[ab_h][ab_s + i];
   const bool arow = (n >> 3) == (q >> 1);   // my A row belongs to my K block's key group
 
   // logit output: tokens 32lg + 2n + nt (nt = 0, 1), token position r0 + nt in its quad with
@@ -473,47 +483,13 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
   // Logits (log2 units) of this wavefront's tile of one block: z[hh][nt] for head
   // 2hp + hh and token tile0 + 32lg + 2n + nt; -inf past the end of the split.
   auto logits = [&](const KBlock4<D> &B, int tile0, float (&z)[2][2]) {
-    // ---- logit A operands of the tile's two key groups (compact build)
-    {
-      const u32x4 *src = reinterpret_cast<const u32x4 *>(&B.ksig[2 * wave + ab_g][ab_s]);
-#pragma unroll
-      for (int o = 0; o < L::SPL / 8; ++o) {
-        const u32x4 sg = src[o];
-        // pairs in octet order (0,2) (1,3) (4,6) (5,7): high part = fp16 of the
-        // product, low part = fp16 of what the high part leaves out
-        uint32_t hw[4], lw[4];
-#pragma unroll
-        for (int pr = 0; pr < 4; ++pr) {
-          // slots ta and ta+2: the same half (ta & 1) of sigma dwords ta>>1 and ta>>1 + 1
-          const int ta = (pr & 2) * 2 + (pr & 1);
-          const float ca = cf[8 * o + ta], cb = cf[8 * o + ta + 2];
-          const uint32_t sa = sg[ta >> 1], sb = sg[(ta >> 1) + 1];
-          uint32_t hh, ll;
-          if (ta & 1) {
-            hh = mixhi<1>(mixlo<1>(ca, sa), cb, sb);
-            ll = reshi<1, 1>(reslo<1, 0>(ca, sa, hh), cb, sb, hh);
-          } else {
-            hh = mixhi<0>(mixlo<0>(ca, sa), cb, sb);
-            ll = reshi<0, 1>(reslo<0, 0>(ca, sa, hh), cb, sb, hh);
-          }
-          hw[pr] = hh;
-          lw[pr] = ll;
-        }
-        u32x4 *dh = reinterpret_cast<u32x4 *>(&W.u.t.abuf[8 * ab_g + 2 * ab_h][ab_s + 8 * o]);
-        u32x4 *dl = reinterpret_cast<u32x4 *>(&W.u.t.abuf[8 * ab_g + 2 * ab_h + 1][ab_s + 8 * o]);
-        *dh = u32x4{hw[0], hw[1], hw[2], hw[3]};
-        *dl = u32x4{lw[0], lw[1], lw[2], lw[3]};
-      }
-    }
-    wave_sync();
-
     // ---- C rows (group lg, heads 2hp, 2hp+1, high/low), columns tokens 32lg + 2n + nt
     f32x4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = acc0, accs = acc0;
     asm volatile("" : "+v"(ones));
     {
       // every K chunk is worked on (slots past |U| have zero codes and zero
       // coefficients): straight-line code without branches between the products
-      const uint16_t *arow_base = arow ? &W.u.t.abuf[n][8 * (q & 1)] : reinterpret_cast<const uint16_t *>(&W.zero);
+      const uint16_t *arow_base = arow ? &B.a[wave][n][8 * (q & 1)] : reinterpret_cast<const uint16_t *>(&W.zero);
       const int astep = arow ? 16 : 0;
 #pragma unroll
       for (int kc = 0; kc < L::NKC; ++kc) {
