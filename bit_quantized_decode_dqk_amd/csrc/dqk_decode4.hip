@@ -247,7 +247,8 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
   using L = Lay4<D>;
   constexpr int G = kG4;
   __shared__ Smem4<D> sm;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: block and tile offsets stay scalar
   // Split-major order: workgroups of one split index run together.
   const int units = c.batch * c.num_kv_heads;
   const int unit = blockIdx.x % units, s = blockIdx.x / units;
