@@ -29,14 +29,20 @@ struct AppendSmem {
   float v2s[kGroup][D / kGroup];  // 2*scale per (token, value group)
 };
 
-__device__ __forceinline__ float load_in(const void *p, bool bf16, size_t i) {
-  return bf16 ? bf16_value(static_cast<const uint16_t *>(p)[i]) : static_cast<const float *>(p)[i];
+template <bool BF16>
+__device__ __forceinline__ float load_in(const void *p, size_t i) {
+  if constexpr (BF16) return bf16_value(static_cast<const uint16_t *>(p)[i]);
+  else return static_cast<const float *>(p)[i];
 }
 
-template <int D>
-__device__ void store_group(const dqk_cache &c, int b, int g, int grp, int L, int n,
-                            const void *k_new, const void *v_new, bool bf16,
-                            const float *__restrict__ bmat, int max_new, AppendSmem<D> &sm) {
+// bcol: this thread's column j = tid % D of B_g, all D rows, loaded at kernel
+// start before anything waits (used by single-token appends; bulk appends
+// stream the rows of B from bmat).
+template <int D, bool BF16>
+__device__ __forceinline__ void store_group(const dqk_cache &c, int b, int g, int grp, int L, int n,
+                                            const void *k_new, const void *v_new,
+                                            const float (&bcol)[D], const float *__restrict__ bmat,
+                                            int max_new, AppendSmem<D> &sm) {
   const int tid = threadIdx.x;
   const int lo = max(L, grp * kGroup);
   const int hi = min(L + n, grp * kGroup + kGroup);
@@ -44,38 +50,51 @@ __device__ void store_group(const dqk_cache &c, int b, int g, int grp, int L, in
   const size_t unit = unit_index(c, b, g);
   const size_t row0 = (unit * (size_t)max_new + (size_t)(lo - L)) * D;
 
-  for (int e = tid; e < cnt * D; e += kThreads) {
-    sm.kx[e / D][e % D] = load_in(k_new, bf16, row0 + e);
-    sm.vx[e / D][e % D] = load_in(v_new, bf16, row0 + e);
+  // The group's value words (two 16-token words per channel, one per thread)
+  // are read now, in flight with the inputs, and rewritten at the end.
+  static_assert(2 * D <= kThreads, "one value word per thread");
+  const int vch = tid % D, vhalf = (tid / D) & 1;
+  const int wlo = grp * kGroup + vhalf * 16;
+  const int va = max(wlo, lo), vz = min(wlo + 16, hi);   // new tokens of this word: [va, vz)
+  uint32_t *wp = c.v_codes + (unit * (size_t)(c.capacity / 16) + (size_t)(wlo >> 4)) * D + vch;
+  const uint32_t wold = *wp;
+
+  // two elements of k and of v per thread in flight; the second index is
+  // clamped to the last element, which is then written twice with the same
+  // value (no branch, so no load waits behind another)
+  for (int e0 = tid; e0 < cnt * D; e0 += 2 * kThreads) {
+    const int e1 = min(e0 + kThreads, cnt * D - 1);
+    const float k0 = load_in<BF16>(k_new, row0 + e0), v0 = load_in<BF16>(v_new, row0 + e0);
+    const float k1 = load_in<BF16>(k_new, row0 + e1), v1 = load_in<BF16>(v_new, row0 + e1);
+    sm.kx[e0 / D][e0 % D] = k0;
+    sm.vx[e0 / D][e0 % D] = v0;
+    sm.kx[e1 / D][e1 % D] = k1;
+    sm.vx[e1 / D][e1 % D] = v1;
   }
   __syncthreads();
 
-  // k' = k B: thread owns output channel j for tokens r0, r0+S, ...; rows of B
-  // are fetched kBRows at a time so that many loads are in flight.
+  // k' = k B: thread owns output channel j for tokens r0, r0+S, ...
   {
     constexpr int S = kThreads / D;           // token slots per channel
     constexpr int R = kGroup / S;             // tokens per thread at most
-    constexpr int kBRows = 16;
     const int j = tid % D, r0 = tid / D;
-    const float *bcol = bmat + (size_t)g * D * D + j;
     if (cnt <= S) {                            // decode-step appends: one token per thread
       float acc = 0.0f;
-      for (int i0 = 0; i0 < D; i0 += kBRows) {
-        float bv[kBRows];
 #pragma unroll
-        for (int r = 0; r < kBRows; ++r) bv[r] = bcol[(size_t)(i0 + r) * D];
-#pragma unroll
-        for (int r = 0; r < kBRows; ++r) acc = __builtin_fmaf(sm.kx[r0][i0 + r], bv[r], acc);
-      }
+      for (int i = 0; i < D; ++i) acc = __builtin_fmaf(sm.kx[r0][i], bcol[i], acc);
       if (r0 < cnt) sm.kp[r0][j] = acc;
     } else {
+      // rows of B fetched kBRows at a time so that many loads are in flight
+      constexpr int kBRows = 16;
+      const float *bc = bmat + (size_t)g * D * D + j;
       float acc[R];
 #pragma unroll
       for (int m = 0; m < R; ++m) acc[m] = 0.0f;
-      for (int i0 = 0; i0 < D; i0 += kBRows) {
+#pragma unroll 1
+      for (int i0 = 0; i0 < D; i0 += kBRows) {   // (a full unroll would spill)
         float bv[kBRows];
 #pragma unroll
-        for (int r = 0; r < kBRows; ++r) bv[r] = bcol[(size_t)(i0 + r) * D];
+        for (int r = 0; r < kBRows; ++r) bv[r] = bc[(size_t)(i0 + r) * D];
 #pragma unroll
         for (int r = 0; r < kBRows; ++r)
 #pragma unroll
@@ -136,28 +155,21 @@ __device__ void store_group(const dqk_cache &c, int b, int g, int grp, int L, in
   }
   __syncthreads();
 
-  // Value codes: the group spans two 16-token words per channel.
-  uint32_t *vw = c.v_codes + unit * (size_t)(c.capacity / 16) * D;
-  for (int e = tid; e < 2 * D; e += kThreads) {
-    const int ch = e % D, half = e / D;
-    const int wlo = grp * kGroup + half * 16;
-    const int a = max(wlo, lo), z = min(wlo + 16, hi);
-    if (a >= z) continue;
-    uint32_t *wp = vw + (size_t)(wlo >> 4) * D + ch;
-    uint32_t w = *wp;
-    for (int p = a; p < z; ++p) {
-      const int sh = 2 * (p & 15);
-      const uint32_t u = code_of(sm.vx[p - lo][ch], sm.v2s[p - lo][ch / kGroup]);
-      w = (w & ~(3u << sh)) | (u << sh);
-    }
-    *wp = w;
+  // Value codes: merge the new tokens' codes into the word read at the start
+  // (a word without new tokens is written back unchanged).
+  uint32_t w = wold;
+  for (int p = va; p < vz; ++p) {
+    const int sh = 2 * (p & 15);
+    const uint32_t u = code_of(sm.vx[p - lo][vch], sm.v2s[p - lo][vch / kGroup]);
+    w = (w & ~(3u << sh)) | (u << sh);
   }
+  if (tid < 2 * D) *wp = w;
   __syncthreads();
 }
 
-template <int D>
+template <int D, bool BF16>
 __global__ __launch_bounds__(kThreads) void append_kernel(dqk_cache c, const void *k_new,
-                                                          const void *v_new, int bf16,
+                                                          const void *v_new,
                                                           const float *__restrict__ bmat,
                                                           const int32_t *__restrict__ n_new,
                                                           int max_new, int blocks_per_unit) {
@@ -165,6 +177,11 @@ __global__ __launch_bounds__(kThreads) void append_kernel(dqk_cache c, const voi
   const int unit = blockIdx.x / blocks_per_unit;
   const int bi = blockIdx.x % blocks_per_unit;
   const int b = unit / c.num_kv_heads, g = unit % c.num_kv_heads;
+  // column tid % D of B_g, in flight together with the length
+  float bcol[D];
+  const float *bp = bmat + (size_t)g * D * D + threadIdx.x % D;
+#pragma unroll
+  for (int i = 0; i < D; ++i) bcol[i] = bp[(size_t)i * D];
   const int L = c.lengths[b];
   const int n = max(0, min(min(n_new[b], max_new), c.capacity - L));
   if (n <= 0) return;
@@ -175,8 +192,8 @@ __global__ __launch_bounds__(kThreads) void append_kernel(dqk_cache c, const voi
   const int ngroups = g1 - g0 + 1;
   if (bi >= ngroups) return;
   if (merged && bi == ngroups - 1) return;
-  store_group<D>(c, b, g, g0 + bi, L, n, k_new, v_new, bf16 != 0, bmat, max_new, sm);
-  if (merged && bi == 0) store_group<D>(c, b, g, g1, L, n, k_new, v_new, bf16 != 0, bmat, max_new, sm);
+  store_group<D, BF16>(c, b, g, g0 + bi, L, n, k_new, v_new, bcol, bmat, max_new, sm);
+  if (merged && bi == 0) store_group<D, BF16>(c, b, g, g1, L, n, k_new, v_new, bcol, bmat, max_new, sm);
 }
 
 __global__ void commit_lengths_kernel(int32_t *lengths, const int32_t *n_new, int batch,
@@ -200,12 +217,21 @@ hipError_t launch_append(const dqk_cache &c, const void *k_new, const void *v_ne
   const int units = c.batch * c.num_kv_heads;
   const int per_unit = (max_new + kGroup - 1) / kGroup + 1;  // a range can straddle one more group
   const dim3 grid((unsigned)(units * per_unit));
-  if (c.head_dim == 64)
-    hipLaunchKernelGGL(append_kernel<64>, grid, dim3(kThreads), 0, s, c, k_new, v_new, (int)bf16,
-                       bmat, n_new, max_new, per_unit);
-  else
-    hipLaunchKernelGGL(append_kernel<128>, grid, dim3(kThreads), 0, s, c, k_new, v_new, (int)bf16,
-                       bmat, n_new, max_new, per_unit);
+  if (c.head_dim == 64) {
+    if (bf16)
+      hipLaunchKernelGGL((append_kernel<64, true>), grid, dim3(kThreads), 0, s, c, k_new, v_new, bmat,
+                         n_new, max_new, per_unit);
+    else
+      hipLaunchKernelGGL((append_kernel<64, false>), grid, dim3(kThreads), 0, s, c, k_new, v_new, bmat,
+                         n_new, max_new, per_unit);
+  } else {
+    if (bf16)
+      hipLaunchKernelGGL((append_kernel<128, true>), grid, dim3(kThreads), 0, s, c, k_new, v_new, bmat,
+                         n_new, max_new, per_unit);
+    else
+      hipLaunchKernelGGL((append_kernel<128, false>), grid, dim3(kThreads), 0, s, c, k_new, v_new, bmat,
+                         n_new, max_new, per_unit);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(commit_lengths_kernel, dim3((c.batch + 255) / 256), dim3(256), 0, s,

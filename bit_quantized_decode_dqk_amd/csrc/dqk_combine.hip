@@ -9,68 +9,102 @@
 namespace dqk {
 namespace {
 
-// One wavefront per (batch row, query head, 32-channel slice).  Lane s merges
-// splits s, s+64, ... on its own (all of its loads are issued before any is
-// used), then the 64 lane results are merged: the maximum and the denominator
-// with cross-lane shuffles, the 32 outputs through LDS.
-constexpr int kSlice = 32;
-constexpr int kCombineLanes = 64;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// One workgroup per (batch row, query head, 32-channel slice).  Thread (k, c)
+// takes float4 column c of the slice and the splits k, k + 32, ... with its own
+// running maximum; a batch of kBatch splits per thread is one round trip (all
+// of its loads are issued before any is used, and a split past the end reads
+// zeros from the range-checked buffer resource, l = 0).  The 32 split classes
+// are then merged by the same rule: four per thread of the first wavefront
+// through LDS, the remaining eight with cross-lane shuffles.
+constexpr int kSlice = 32;                       // channels per workgroup
+constexpr int kCols = kSlice / 4;                // float4 columns
+constexpr int kThreadsC = 256;
+constexpr int kClasses = kThreadsC / kCols;      // 32 split classes
+constexpr int kBatch = 4;
+constexpr int kRsrcWord3C = 0x00020000;          // raw buffer, 32-bit elements, range-checked
+
+struct State {
+  float m, l;
+  f32x4 o;
+};
+
+// (m, l, o) of two disjoint sets of splits -> their union (m = -inf: empty).
+__device__ __forceinline__ State join(State a, State b) {
+  const float M = fmaxf(a.m, b.m);
+  if (M == -INFINITY) return a;
+  const float fa = exp2f(a.m - M), fb = exp2f(b.m - M);   // 0 for an empty side
+  return State{M, a.l * fa + b.l * fb, a.o * fa + b.o * fb};
+}
+
+__device__ __forceinline__ State shfl_state(State s, int off) {
+  State r;
+  r.m = __shfl_xor(s.m, off, 64);
+  r.l = __shfl_xor(s.l, off, 64);
+  r.o.x = __shfl_xor(s.o.x, off, 64);
+  r.o.y = __shfl_xor(s.o.y, off, 64);
+  r.o.z = __shfl_xor(s.o.z, off, 64);
+  r.o.w = __shfl_xor(s.o.w, off, 64);
+  return r;
+}
 
 template <int D>
-__global__ __launch_bounds__(kCombineLanes) void combine_kernel(const float *__restrict__ ws,
-                                                                int hq, int hkv, int nsplit,
-                                                                float *__restrict__ out) {
+__global__ __launch_bounds__(kThreadsC) void combine_kernel(const float *__restrict__ ws, int hq,
+                                                            int hkv, int nsplit,
+                                                            float *__restrict__ out) {
   constexpr int NSL = D / kSlice;
-  __shared__ float part[kCombineLanes][kSlice + 1];
+  constexpr int PH = D + kPartialHead;   // floats per (split, head)
+  __shared__ State part[kThreadsC];
   const int row = blockIdx.x / NSL, sl = blockIdx.x % NSL;
   const int b = row / hq, h = row % hq;
   const int G = hq / hkv;
   const int unit = b * hkv + h / G, hi = h % G;
-  const int lane = threadIdx.x;
-  const size_t stride = (size_t)G * (D + kPartialHead);
-  const float *base = ws + ((size_t)unit * nsplit * G + hi) * (D + kPartialHead);
+  const int tid = threadIdx.x, c = tid % kCols, k = tid / kCols;
+  const float *base = ws + ((size_t)unit * nsplit * G + hi) * PH;
+  const int span = ((nsplit - 1) * G + 1) * PH;   // floats from base to the last split's end
+  const auto r = __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, span * (int)sizeof(float),
+                                                   kRsrcWord3C);
+  const uint32_t stride = (uint32_t)G * PH * 4u;   // bytes between splits
+  const uint32_t col = (uint32_t)(kPartialHead + kSlice * sl + 4 * c) * 4u;
 
-  float m = -INFINITY, l = 0.0f;
-  float o[kSlice];
+  State st{-INFINITY, 0.0f, {0.0f, 0.0f, 0.0f, 0.0f}};
+  for (int s0 = k; s0 < nsplit; s0 += kClasses * kBatch) {
+    f32x2 ml[kBatch];
+    f32x4 o[kBatch];
 #pragma unroll
-  for (int c = 0; c < kSlice; ++c) o[c] = 0.0f;
-  for (int s = lane; s < nsplit; s += kCombineLanes) {
-    const float *p = base + s * stride;
-    const float ms = p[0], ls = p[1];
-    float4 v[kSlice / 4];
+    for (int j = 0; j < kBatch; ++j) {
+      const uint32_t at = (uint32_t)(s0 + kClasses * j) * stride;
+      ml[j] = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(r, at, 0, 0));
+      o[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, at + col, 0, 0));
+    }
+    float bm = st.m;
 #pragma unroll
-    for (int c = 0; c < kSlice / 4; ++c)
-      v[c] = *reinterpret_cast<const float4 *>(p + kPartialHead + kSlice * sl + 4 * c);
-    if (ls > 0.0f) {
-      const float mn = fmaxf(m, ms);
-      const float fa = exp2f(m - mn), fb = exp2f(ms - mn);
-      l = l * fa + ls * fb;
+    for (int j = 0; j < kBatch; ++j) bm = ml[j].y > 0.0f ? fmaxf(bm, ml[j].x) : bm;
+    const float f = st.m == -INFINITY ? 0.0f : exp2f(st.m - bm);   // l and o are 0 while m is -inf
+    st.l *= f;
+    st.o *= f;
+    st.m = bm;
 #pragma unroll
-      for (int c = 0; c < kSlice / 4; ++c) {
-        o[4 * c + 0] = o[4 * c + 0] * fa + v[c].x * fb;
-        o[4 * c + 1] = o[4 * c + 1] * fa + v[c].y * fb;
-        o[4 * c + 2] = o[4 * c + 2] * fa + v[c].z * fb;
-        o[4 * c + 3] = o[4 * c + 3] * fa + v[c].w * fb;
-      }
-      m = mn;
+    for (int j = 0; j < kBatch; ++j) {
+      const float w = ml[j].y > 0.0f ? exp2f(ml[j].x - bm) : 0.0f;   // a partial's o is finite
+      st.l = fmaf(w, ml[j].y, st.l);
+      st.o += w * o[j];
     }
   }
-  float M = m;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
-  const float f = l > 0.0f ? exp2f(m - M) : 0.0f;
-  float L = l * f;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off, 64);
-#pragma unroll
-  for (int c = 0; c < kSlice; ++c) part[lane][c] = o[c] * f;
+  part[tid] = st;
   __syncthreads();
-  if (lane < kSlice) {
-    float acc = 0.0f;
-#pragma unroll 8
-    for (int s = 0; s < kCombineLanes; ++s) acc += part[s][lane];
-    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-    out[(size_t)row * D + kSlice * sl + lane] = acc * inv;
+  if (tid >= 64) return;
+  // thread (k < 8, c) of the first wavefront joins classes k, k + 8, k + 16, k + 24
+#pragma unroll
+  for (int q = 1; q < kClasses / 8; ++q) st = join(st, part[tid + 64 * q]);
+  // lanes k * 8 + c: join over k with shuffles across lane bits 3-5
+#pragma unroll
+  for (int off = 8; off < 64; off <<= 1) st = join(st, shfl_state(st, off));
+  if (k == 0) {
+    const float inv = st.l > 0.0f ? 1.0f / st.l : 0.0f;
+    *reinterpret_cast<f32x4 *>(out + (size_t)row * D + kSlice * sl + 4 * c) = st.o * inv;
   }
 }
 
@@ -80,9 +114,9 @@ hipError_t launch_combine(const float *ws, int batch, int hq, int hkv, int d, in
                           float *out, hipStream_t s) {
   const dim3 grid((unsigned)(batch * hq * (d / kSlice)));
   if (d == 64)
-    hipLaunchKernelGGL(combine_kernel<64>, grid, dim3(kCombineLanes), 0, s, ws, hq, hkv, nsplit, out);
+    hipLaunchKernelGGL(combine_kernel<64>, grid, dim3(kThreadsC), 0, s, ws, hq, hkv, nsplit, out);
   else
-    hipLaunchKernelGGL(combine_kernel<128>, grid, dim3(kCombineLanes), 0, s, ws, hq, hkv, nsplit, out);
+    hipLaunchKernelGGL(combine_kernel<128>, grid, dim3(kThreadsC), 0, s, ws, hq, hkv, nsplit, out);
   return hipGetLastError();
 }
 

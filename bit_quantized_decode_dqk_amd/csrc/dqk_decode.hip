@@ -587,10 +587,9 @@ hipError_t launch_decode_d(const dqk_cache &c, const float *qp, const int32_t *s
     case 4: {
       if (!decode4_supported(c))
         return launch_decode_t<D, 4>(c, qp, sel, hq, keep, scale2, split, out, ws, s);
-      const int nsplit = num_splits(c.capacity, split);
-      const hipError_t e = launch_decode4(c, qp, sel, hq, keep, scale2, nsplit, ws, s);
+      const hipError_t e = launch_decode4(c, qp, sel, hq, keep, scale2, split, ws, s);
       if (e != hipSuccess) return e;
-      return launch_combine(ws, c.batch, hq, c.num_kv_heads, D, nsplit, out, s);
+      return launch_combine(ws, c.batch, hq, c.num_kv_heads, D, num_splits(c.capacity, split), out, s);
     }
     default: return launch_decode_t<D, 8>(c, qp, sel, hq, keep, scale2, split, out, ws, s);
   }

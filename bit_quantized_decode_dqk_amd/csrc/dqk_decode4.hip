@@ -64,6 +64,8 @@ constexpr int kTile4 = 64;          // tokens per wavefront tile: two key groups
 constexpr int kBlock4 = kTile4 * kWaves4;   // tokens per workgroup block
 constexpr int kKsPerBlock = kBlock4 / kGroup;   // key groups per block
 constexpr int kChunk4 = 8;          // blocks per chunk: logits of a chunk stay in registers
+// a ninth block of a chunk reuses key stage 0 / LDS buffer 0 and value stage 2
+static_assert(kChunk4 % 2 == 0 && kChunk4 % 3 == 2, "ninth block stages");
 constexpr uint32_t kOneF16x2 = 0x3C003C00u;
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit elements, range-checked (gfx9)
 constexpr uint32_t kFar = 0x40000000u;   // offset past every plane: the load returns zero
@@ -243,7 +245,8 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
                                                                const float *__restrict__ qp,
                                                                const int32_t *__restrict__ sel,
                                                                int hq, int keep, float scale2,
-                                                               int nsplit, float *__restrict__ ws) {
+                                                               int nsplit, int bps,
+                                                               float *__restrict__ ws) {
   using L = Lay4<D>;
   constexpr int G = kG4;
   __shared__ Smem4<D> sm;
@@ -267,8 +270,10 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
   }
   const int len = max(0, min(c.lengths[b], c.capacity));
   const int nblk_all = (len + kBlock4 - 1) / kBlock4;
-  const int blo = (int)(((long long)s * nblk_all) / nsplit);
-  const int bhi = (int)(((long long)(s + 1) * nblk_all) / nsplit);
+  // bps > 0: split s is blocks [s bps, (s + 1) bps) of the row; else the row's
+  // blocks are shared out evenly over the nsplit splits
+  const int blo = bps > 0 ? min(s * bps, nblk_all) : (int)(((long long)s * nblk_all) / nsplit);
+  const int bhi = bps > 0 ? min(blo + bps, nblk_all) : (int)(((long long)(s + 1) * nblk_all) / nsplit);
   const int t_begin = blo * kBlock4;
   const int t_end = min(bhi * kBlock4, len);
   const int nb = bhi - blo;
@@ -329,16 +334,35 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
   }
   // Tokens of the unfinished last key group (only in the workgroup that reaches
   // it): exact logits from the fp32 tail keys, one per (head, token).
+  // The tail rows are staged in LDS first (the key block buffers are free until
+  // the first block): one round trip instead of one per channel.
+  // Every channel is summed in ascending order: a channel the head drops has
+  // coefficient 0 and adds exactly nothing.  Rows are padded to D + 4 floats so
+  // that the rows of a wavefront's lanes fall in different LDS banks.
   if (t_body < t_end) {
+    constexpr int TS = D + 4;
+    static_assert(sizeof(sm.kb[0]) >= sizeof(float) * kGroup * TS, "tail rows fit a key block buffer");
+    float *trow = reinterpret_cast<float *>(&sm.kb[0]);
+#pragma unroll
+    for (int k = 0; k < kGroup * D / (4 * kThreads4); ++k) {
+      const int e = 4 * (tid + kThreads4 * k);
+      *reinterpret_cast<f32x4 *>(trow + (e / D) * TS + e % D) = *reinterpret_cast<const f32x4 *>(tail + e);
+    }
+    const int h = (tid / kGroup) % G, r = tid % kGroup, t = t_body + r;
+    const float c0 = f16_value(c0row[min(t, t_end - 1)]);
+    __syncthreads();
     if (tid < G * kGroup) {
-      const int h = tid / kGroup, r = tid % kGroup, t = t_body + r;
       float zz = -INFINITY;
       if (t < t_end) {
-        zz = sm.coefc[h][0] * f16_value(c0row[t]);
-        const float *row = tail + (size_t)r * D;
-        for (int i = 0; i < nu; ++i) {
-          const int ch = sm.ulist[i];
-          zz = fmaf(sm.coefc[h][ch], row[ch], zz);
+        zz = sm.coefc[h][0] * c0;   // channel 0: its fp16 value, as in the blocks
+#pragma unroll
+        for (int c4 = 0; c4 < D; c4 += 4) {
+          const f32x4 cf = *reinterpret_cast<const f32x4 *>(&sm.coefc[h][c4]);
+          const f32x4 x = *reinterpret_cast<const f32x4 *>(&trow[r * TS + c4]);
+          if (c4 > 0) zz = fmaf(cf.x, x.x, zz);
+          zz = fmaf(cf.y, x.y, zz);
+          zz = fmaf(cf.z, x.z, zz);
+          zz = fmaf(cf.w, x.w, zz);
         }
       }
       sm.tailz[h][r] = zz;
@@ -676,11 +700,14 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
   };
 
   // ---------------------------------------------------------------- chunks
-  for (int cb = 0; cb < nb; cb += kChunk4) {
+  for (int cb = 0; cb < nb;) {
     // a wavefront that is through with the previous chunk waits here until the
     // others have also read the key blocks of its last two blocks
     if (cb > 0) block_barrier();
-    const int nbc = min(kChunk4, nb - cb);           // blocks in this chunk
+    // blocks in this chunk: up to eight, or nine when nine are left (the ninth
+    // takes the same steps after the first eight, with logits of its own), so
+    // that a share of just over eight blocks costs one block, not one chunk
+    const int nbc = nb - cb == kChunk4 + 1 ? kChunk4 + 1 : min(kChunk4, nb - cb);
     const int c_t0 = t_begin + kBlock4 * cb;         // first token of the chunk
     float zs[kChunk4][2][2];                         // this wavefront's logits of the chunk
     float zl[2] = {-INFINITY, -INFINITY};            // and their maximum per head of the pair
@@ -709,6 +736,20 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
       }
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) zl[hh] = fmaxf(zl[hh], fmaxf(zs[i][hh][0], zs[i][hh][1]));
+    }
+    float z9[2][2];   // the ninth block (stage S0 and LDS buffer 0, as block 8 of the loop would use)
+    if (nbc > kChunk4) {
+      const int p0 = c_t0 + kBlock4 * kChunk4;
+      kcommit(S0, sm.kb[0], p0);
+      block_barrier();
+      const int tile0 = p0 + kTile4 * wave;
+      if (tile0 < t_end) {
+        logits(sm.kb[0], tile0, z9);
+      } else {
+        z9[0][0] = z9[0][1] = z9[1][0] = z9[1][1] = -INFINITY;
+      }
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) zl[hh] = fmaxf(zl[hh], fmaxf(z9[hh][0], z9[hh][1]));
     }
 
     // ---- pass 2: values; the first three tiles are on their way during the maximum
@@ -769,6 +810,11 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
       if (tile0 < t_end) values(V, tile0, zs[i], mr);
       vissue(V, tile0 + 3 * kBlock4, i + 3 < nbc);
     }
+    if (nbc > kChunk4) {   // the ninth block's values are in stage V2 (8 % 3 == 2)
+      const int tile0 = c_t0 + kBlock4 * kChunk4 + kTile4 * wave;
+      if (tile0 < t_end) values(V2, tile0, z9, mr);
+    }
+    cb += nbc;
   }
   // loads of tiles past the end (they return zeros) land before the merge
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -805,14 +851,12 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
     const float inv_f = ldexpf(1.0f, -f_run);
 #pragma unroll
     for (int hf = 0; hf < L::NH; ++hf) {
-      const int ch = 64 * hf + 16 * q + n;
-      const int j = ch / 32;   // 2 hf + (q >> 1)
+      const int ch = 64 * hf + 16 * q + n;   // value group 2 hf + (q >> 1)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float si = (q >> 1) ? sh[i][2 * hf + 1] : sh[i][2 * hf];
+        const float si = sel2((q >> 1) != 0, sh[i][2 * hf], sh[i][2 * hf + 1]);
         W.u.merge[i][ch] = (2.0f * vacc[hf][i] - 3.0f * si) * inv_f;
       }
-      (void)j;
     }
 #pragma unroll
     for (int h = 0; h < G; ++h)
@@ -850,13 +894,18 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
 bool decode4_supported(const dqk_cache &c) { return c.capacity % 64 == 0; }
 
 hipError_t launch_decode4(const dqk_cache &c, const float *q_prime, const int32_t *sel_idx, int hq,
-                          int keep, float scale2, int nsplit, float *ws, hipStream_t s) {
+                          int keep, float scale2, int split, float *ws, hipStream_t s) {
+  const int nsplit = num_splits(c.capacity, split);
+  // a split of whole blocks covers exactly its split tokens of every row
+  const int bps = split % kBlock4 == 0 ? split / kBlock4 : 0;
   const int items = c.batch * c.num_kv_heads * nsplit;
   const dim3 grid((unsigned)items), block(kThreads4);
   if (c.head_dim == 64)
-    hipLaunchKernelGGL((decode4_kernel<64>), grid, block, 0, s, c, q_prime, sel_idx, hq, keep, scale2, nsplit, ws);
+    hipLaunchKernelGGL((decode4_kernel<64>), grid, block, 0, s, c, q_prime, sel_idx, hq, keep, scale2, nsplit,
+                       bps, ws);
   else
-    hipLaunchKernelGGL((decode4_kernel<128>), grid, block, 0, s, c, q_prime, sel_idx, hq, keep, scale2, nsplit, ws);
+    hipLaunchKernelGGL((decode4_kernel<128>), grid, block, 0, s, c, q_prime, sel_idx, hq, keep, scale2, nsplit,
+                       bps, ws);
   return hipGetLastError();
 }
 

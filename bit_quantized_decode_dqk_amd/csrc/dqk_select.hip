@@ -20,7 +20,6 @@ namespace dqk {
 namespace {
 
 constexpr int kThreads = 128;
-constexpr int kBatchRows = 16;   // rows of A loaded per batch (independent loads in flight)
 
 __device__ __forceinline__ int popc(unsigned long long m) { return __popcll(m); }
 
@@ -62,8 +61,8 @@ __device__ void select_one_head(const float *mag, int keep, int32_t *idx) {
 // One workgroup per (batch row, KV head); the G query heads of the group share
 // every load of A_g.  Lane j forms q'_j of all G heads; each wavefront then
 // selects for every other head.
-template <int D, int G>
-__global__ __launch_bounds__(kThreads) void select_kernel(const void *q, int bf16,
+template <int D, int G, bool BF16>
+__global__ __launch_bounds__(kThreads) void select_kernel(const void *q,
                                                           const float *__restrict__ amat, int hq,
                                                           int hkv, int keep, float *q_prime,
                                                           int32_t *sel_idx) {
@@ -72,24 +71,36 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const void *q, int bf1
   const int b = blockIdx.x / hkv, g = blockIdx.x % hkv;
   const size_t row0 = (size_t)b * hq + (size_t)g * G;
   const int j = threadIdx.x, wave = j >> 6;
-  for (int e = j; e < G * D; e += kThreads)
-    qs[e / D][e % D] = bf16 ? bf16_value(static_cast<const uint16_t *>(q)[row0 * D + e])
-                            : static_cast<const float *>(q)[row0 * D + e];
+  // The query rows and lane j's whole column of A_g are loaded together: the
+  // setup is one round trip.
+  constexpr int QJ = (G * D + kThreads - 1) / kThreads;
+  float qv[QJ];
+#pragma unroll
+  for (int k = 0; k < QJ; ++k) {
+    const int e = min(j + kThreads * k, G * D - 1);   // unconditional loads (no branch between them)
+    if constexpr (BF16)
+      qv[k] = bf16_value(static_cast<const uint16_t *>(q)[row0 * D + e]);
+    else
+      qv[k] = static_cast<const float *>(q)[row0 * D + e];
+  }
+  float a[D];
+  const float *acol = amat + (size_t)g * D * D + (j < D ? j : 0);
+#pragma unroll
+  for (int r = 0; r < D; ++r) a[r] = acol[(size_t)r * D];
+#pragma unroll
+  for (int k = 0; k < QJ; ++k) {
+    const int e = j + kThreads * k;
+    if (e < G * D) qs[e / D][e % D] = qv[k];
+  }
   __syncthreads();
   if (j < D) {
     float acc[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) acc[h] = 0.0f;
-    const float *acol = amat + (size_t)g * D * D + j;
-    for (int i0 = 0; i0 < D; i0 += kBatchRows) {
-      float a[kBatchRows];
 #pragma unroll
-      for (int r = 0; r < kBatchRows; ++r) a[r] = acol[(size_t)(i0 + r) * D];
+    for (int r = 0; r < D; ++r)
 #pragma unroll
-      for (int r = 0; r < kBatchRows; ++r)
-#pragma unroll
-        for (int h = 0; h < G; ++h) acc[h] = __builtin_fmaf(qs[h][i0 + r], a[r], acc[h]);
-    }
+      for (int h = 0; h < G; ++h) acc[h] = __builtin_fmaf(qs[h][r], a[r], acc[h]);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       q_prime[(row0 + h) * D + j] = acc[h];
@@ -100,15 +111,24 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const void *q, int bf1
   for (int h = wave; h < G; h += kThreads / 64) select_one_head<D>(mag[h], keep, sel_idx + (row0 + h) * keep);
 }
 
+template <int D, int G>
+void launch_g(const void *q, bool bf16, const float *amat, int batch, int hq, int hkv, int keep,
+              float *q_prime, int32_t *sel_idx, hipStream_t s) {
+  const dim3 grid((unsigned)(batch * hkv));
+  if (bf16)
+    hipLaunchKernelGGL((select_kernel<D, G, true>), grid, dim3(kThreads), 0, s, q, amat, hq, hkv, keep, q_prime, sel_idx);
+  else
+    hipLaunchKernelGGL((select_kernel<D, G, false>), grid, dim3(kThreads), 0, s, q, amat, hq, hkv, keep, q_prime, sel_idx);
+}
+
 template <int D>
 hipError_t launch_d(const void *q, bool bf16, const float *amat, int batch, int hq, int hkv,
                     int keep, float *q_prime, int32_t *sel_idx, hipStream_t s) {
-  const dim3 grid((unsigned)(batch * hkv));
   switch (hq / hkv) {
-    case 1: hipLaunchKernelGGL((select_kernel<D, 1>), grid, dim3(kThreads), 0, s, q, (int)bf16, amat, hq, hkv, keep, q_prime, sel_idx); break;
-    case 2: hipLaunchKernelGGL((select_kernel<D, 2>), grid, dim3(kThreads), 0, s, q, (int)bf16, amat, hq, hkv, keep, q_prime, sel_idx); break;
-    case 4: hipLaunchKernelGGL((select_kernel<D, 4>), grid, dim3(kThreads), 0, s, q, (int)bf16, amat, hq, hkv, keep, q_prime, sel_idx); break;
-    case 8: hipLaunchKernelGGL((select_kernel<D, 8>), grid, dim3(kThreads), 0, s, q, (int)bf16, amat, hq, hkv, keep, q_prime, sel_idx); break;
+    case 1: launch_g<D, 1>(q, bf16, amat, batch, hq, hkv, keep, q_prime, sel_idx, s); break;
+    case 2: launch_g<D, 2>(q, bf16, amat, batch, hq, hkv, keep, q_prime, sel_idx, s); break;
+    case 4: launch_g<D, 4>(q, bf16, amat, batch, hq, hkv, keep, q_prime, sel_idx, s); break;
+    case 8: launch_g<D, 8>(q, bf16, amat, batch, hq, hkv, keep, q_prime, sel_idx, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

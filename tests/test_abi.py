@@ -79,6 +79,29 @@ def test_cache_validation_without_gpu():
     assert L.dqk_decode_workspace_bytes(None, 8, 0, C.byref(out)) == INVALID
 
 
+def test_default_split_for_groups_of_four():
+    """Default split of the four-head decode, read back through the workspace
+    size (one partial of 4 heads x (d + 4) floats per split and (row, KV head)):
+    about 512 workgroups (two per compute unit on 256), at least 256 tokens of
+    capacity each."""
+    L = M.lib()
+    out = C.c_size_t(0)
+
+    def splits(batch, hkv, cap):
+        c = fake_cache(batch=batch, num_kv_heads=hkv, capacity=cap)
+        assert L.dqk_decode_workspace_bytes(C.byref(c), 4 * hkv, 0, C.byref(out)) == OK
+        per = batch * hkv * 4 * 132 * 4
+        assert out.value % per == 0
+        return out.value // per
+
+    assert splits(1, 8, 131072) == 64
+    assert splits(1, 8, 131328) == 64          # 513 blocks: one split of nine
+    assert splits(1, 8, 131072 + 768) == 64
+    assert splits(1, 8, 32768) == 64           # 128 blocks: 2 per split
+    assert splits(4, 8, 8192) == 16            # 32 units x 16 splits of 2 blocks
+    assert splits(1, 1, 512) == 2              # at least 256 tokens per split
+
+
 def test_decode_validation_without_gpu():
     L = M.lib()
     c = C.byref(fake_cache())

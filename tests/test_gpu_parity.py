@@ -8,6 +8,7 @@ span several splits and a ragged tail.
 """
 import numpy as np
 import pytest
+import torch
 
 import bit_quantized_decode_dqk_amd as M
 import workloads as W
@@ -220,6 +221,106 @@ def test_decode_group4_many_blocks(orc, d, lens, cap):
     decode_case(orc, wl, splits=(0, 64, 512, 1024, cap))
     decode_case(orc, wl, sparsity=0, sm_mult=0.02, splits=(0, 256))
     decode_case(orc, wl, sparsity=60, sm_mult=0.05, splits=(0,))
+
+
+def test_decode_group4_nine_block_chunks(orc):
+    """Shares of nine 256-token blocks run as one chunk of nine (a row of 2304
+    tokens, a ragged one of 2200 with its tail, one of 4300 split 8 + 9), with
+    one split per row, whole-block splits of nine blocks, and the default."""
+    wl = W.custom("g4-nine", 31, 3, 32, 8, 128, [2304, 2200, 4300], 4352, "bf16",
+                  log_uniform_key_scales=True)
+    decode_case(orc, wl, splits=(4352, 2304, 0))
+
+
+@pytest.mark.parametrize("hq,hkv,lens", [(4, 1, [3000, 1200, 64]), (12, 3, [2500]),
+                                          (20, 5, [1800, 4000])])
+def test_decode_group4_unit_counts(orc, hq, hkv, lens):
+    """Groups of four with (row, KV head) counts that are not multiples of
+    eight: the splits of one row and KV head run on different parts of the chip,
+    and the last to finish merges the others' partials."""
+    wl = W.custom(f"g4-u{hkv}", 30 + hkv, len(lens), hq, hkv, 128, lens, 4032, "bf16",
+                  log_uniform_key_scales=True)
+    decode_case(orc, wl, splits=(0, 64, 256, 1024))
+
+
+def test_decode_workspace_reuse(orc):
+    """One caller-provided workspace serves calls with different split counts
+    and then a smaller cache: each output is bitwise the one a fresh workspace
+    gives (nothing carries over between calls)."""
+    wl = W.custom("g4-reuse", 28, 3, 32, 8, 128, [5000, 2049, 257], 5056, "bf16",
+                  log_uniform_key_scales=True)
+    g, a, b, k, v = build_gpu(wl)
+    qp, idx = gpu_queries(wl, W.queries(wl), a, 77)
+    sm = W.default_sm_scale(wl.d)
+    splits = (0, 64, 512, 1024, 5056, 64, 0)
+    nb = max(M.decode_workspace_bytes(g, wl.hq, sp) for sp in splits)
+    ws = torch.full((nb,), 0xFF, dtype=torch.uint8, device="cuda")   # NaN bit patterns
+    for sp in splits:
+        say("workspace reuse, split", sp)
+        fresh = M.decode_attention(g, qp, idx, sm, split_tokens=sp).cpu().numpy()
+        out = torch.empty((wl.batch, wl.hq, wl.d), dtype=torch.float32, device="cuda")
+        M.decode_attention(g, qp, idx, sm, sp, out, ws)
+        assert np.array_equal(fresh.view(np.uint32), out.cpu().numpy().view(np.uint32)), sp
+    wl1 = W.custom("g4-reuse1", 29, 1, 32, 8, 128, [3000], 5056, "bf16")
+    g1, a1, _, _, _ = build_gpu(wl1)
+    qp1, idx1 = gpu_queries(wl1, W.queries(wl1), a1, 77)
+    fresh = M.decode_attention(g1, qp1, idx1, sm).cpu().numpy()
+    out = torch.empty((1, wl1.hq, wl1.d), dtype=torch.float32, device="cuda")
+    M.decode_attention(g1, qp1, idx1, sm, 0, out, ws)
+    assert np.array_equal(fresh.view(np.uint32), out.cpu().numpy().view(np.uint32))
+
+
+def test_decode_ctx128k_sampled(orc):
+    """The benchmark's workload at full size (batch 1, 32/8 heads, head_dim 128,
+    131072 tokens, 40% sparsity) in its launch configuration (the default
+    split), at exactly 128K tokens, one past (a remainder split of one token)
+    and 33 past (a full key group and a tail token in the remainder split).
+    KV heads 0 and 5 are checked: the oracle decodes each from a one-KV-head
+    cache of that head's keys and values (the units are independent), built by
+    the same appends."""
+    wl = W.workload("ctx128k", steps=256)
+    ctx, sm = int(wl.ctx[0]), W.default_sm_scale(wl.d)
+    extras = (0, 1, 33)
+    n_all = ctx + extras[-1]
+    a, b = W.transforms(wl)
+    kscale = W.key_scales(wl)
+    say("ctx128k sampled: generating", n_all, "tokens x", wl.hkv, "KV heads")
+    kb = np.zeros((1, wl.hkv, n_all, wl.d), dtype=np.uint16)
+    vb = np.zeros_like(kb)
+    sampled = {0: None, 5: None}
+    for g in range(wl.hkv):
+        kk, vv = W.unit_kv(wl, 0, g, 0, n_all, kscale)
+        kb[0, g], vb[0, g] = W.bf16_bits(kk), W.bf16_bits(vv)
+        if g in sampled:
+            sampled[g] = (kk, vv)
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+    cache = M.Cache(1, wl.hkv, wl.d, wl.cap)
+    bm = dev_f32(b)
+    ocs = {g: orc.Cache(1, 1, wl.d, wl.cap) for g in sampled}
+    keep = orc.keep_count(wl.d, 40)
+    q = W.queries(wl)
+    qp, idx = gpu_queries(wl, q, a, keep)
+    idx_np = idx.cpu().numpy()
+    pos = 0
+    for extra in extras:
+        n = ctx + extra - pos
+        say(f"  append {n} tokens (length {ctx + extra})")
+        M.transform_quantize_append(cache, to_dev(kb[:, :, pos:pos + n]), to_dev(vb[:, :, pos:pos + n]),
+                                    bm, dev_i32(np.array([n], dtype=np.int32)))
+        for g, (kk, vv) in sampled.items():
+            ocs[g].append(kk[None, None, pos:pos + n], vv[None, None, pos:pos + n], b[g:g + 1], [n])
+        pos += n
+        out = M.decode_attention(cache, qp, idx, sm).cpu().numpy()
+        for g in sampled:
+            hs = slice(4 * g, 4 * g + 4)
+            qpo, idxo = orc.queries(q[:, hs], a[g:g + 1], 1, keep)
+            assert np.array_equal(idx_np[:, hs], idxo), g
+            err = rel_err(out[:, hs], ocs[g].decode(qpo, idxo, sm))
+            say(f"  length {ctx + extra}, KV head {g}: max rel err {err:.3e}")
+            assert err <= REL_TOL, (extra, g, err)
 
 
 def test_decode_poisoned_dropped_channels(orc):
