@@ -64,7 +64,7 @@ constexpr int kTile4 = 64;          // tokens per wavefront tile: two key groups
 constexpr int kBlock4 = kTile4 * kWaves4;   // tokens per workgroup block
 constexpr int kKsPerBlock = kBlock4 / kGroup;   // key groups per block
 constexpr int kChunk4 = 8;          // blocks per chunk: logits of a chunk stay in registers
-// a ninth block of a chunk reuses key stage 0 / LDS buffer 0 and value stage 2
+// a ninth block of a chunk is committed to LDS buffer 0 and uses value stage 2
 static_assert(kChunk4 % 2 == 0 && kChunk4 % 3 == 2, "ninth block stages");
 constexpr uint32_t kOneF16x2 = 0x3C003C00u;
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit elements, range-checked (gfx9)
@@ -85,8 +85,13 @@ template <int D>
 struct __attribute__((aligned(16))) KBlock4 {
   uint32_t y[kWaves4][Lay4<D>::OCT][16][2];   // key codes: tile, slot octet, token quad, slots 0-3 | 4-7
   // logit A operands of tile w: rows 8g + 2h + limb (key group g of the tile,
-  // head h, fp16 high/low part), slots in octet order 0,2,1,3,4,6,5,7
-  uint16_t a[kWaves4][16][Lay4<D>::AROW];
+  // head h, fp16 high/low part), slots in octet order 0,2,1,3,4,6,5,7.  The
+  // tiles are 8 dwords apart modulo the 32 LDS banks, so that the four tiles
+  // of one A-building write land in different banks.
+  struct {
+    uint16_t r[16][Lay4<D>::AROW];
+    uint16_t pad[16];
+  } a[kWaves4];
   uint32_t c0w[kThreads4];                    // key channel 0: fp16 pair of tokens 2i, 2i+1 (i < 128)
 };
 
@@ -95,7 +100,10 @@ struct __attribute__((aligned(16))) WaveSmem4 {
   u32x4 zero;   // a 16-byte zero operand
   union {
     struct {
-      uint16_t pbuf[Lay4<D>::VG][2][kG4][4][8];   // value A: group j, K chunk, head, word, K position
+      // value A: group j, K chunk kc, then word w, head h, 8 K positions at
+      // ((w * 4 + h) * 8 + k); each (j, kc) slab is padded by 4 dwords so that
+      // neither the 2-byte writes nor the 16-byte reads meet in an LDS bank
+      uint16_t pbuf[Lay4<D>::VG][2][4 * kG4 * 8 + 8];
     } t;
     float merge[kG4][D];                          // the wavefront's output at the end of the split
   } u;
@@ -469,7 +477,7 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
       uint32_t lo0 = reshi<0, 1>(reslo<0, 0>(ca[h], v0, hi0), cb[h], v1, hi0);
       uint32_t hi1 = mixhi<1>(mixlo<1>(ca[h], v0), cb[h], v1);
       uint32_t lo1 = reshi<1, 1>(reslo<1, 0>(ca[h], v0, hi1), cb[h], v1, hi1);
-      uint16_t (*ar)[L::AROW] = B.a[agp];
+      uint16_t (*ar)[L::AROW] = B.a[agp].r;
       *reinterpret_cast<uint32_t *>(&ar[2 * h][8 * aoct + 2 * am]) = hi0;
       *reinterpret_cast<uint32_t *>(&ar[2 * h + 1][8 * aoct + 2 * am]) = lo0;
       *reinterpret_cast<uint32_t *>(&ar[8 + 2 * h][8 * aoct + 2 * am]) = hi1;
@@ -514,7 +522,7 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
     {
       // every K chunk is worked on (slots past |U| have zero codes and zero
       // coefficients): straight-line code without branches between the products
-      const uint16_t *arow_base = arow ? &B.a[wave][n][8 * (q & 1)] : reinterpret_cast<const uint16_t *>(&W.zero);
+      const uint16_t *arow_base = arow ? &B.a[wave].r[n][8 * (q & 1)] : reinterpret_cast<const uint16_t *>(&W.zero);
       const int astep = arow ? 16 : 0;
 #pragma unroll
       for (int kc = 0; kc < L::NKC; ++kc) {
@@ -672,7 +680,7 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
       const uint32_t s0 = cvs[j >> 1], s1 = cvs[L::VG / 2 + (j >> 1)];
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        uint16_t *dst = &W.u.t.pbuf[j][pkc][2 * hp + hh][pw][pi0];
+        uint16_t *dst = &W.u.t.pbuf[j][pkc][(pw * 4 + 2 * hp + hh) * 8 + pi0];
         const uint32_t a0 = (j & 1) ? mixlo<1>(p[hh][0], s0) : mixlo<0>(p[hh][0], s0);
         const uint32_t a1 = (j & 1) ? mixlo<1>(p[hh][1], s1) : mixlo<0>(p[hh][1], s1);
         dst[0] = (uint16_t)a0;
@@ -692,7 +700,7 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
       for (int wr = 0; wr < 4; ++wr)
 #pragma unroll
         for (int kc2 = 0; kc2 < 2; ++kc2) {
-          const u32x4 *src = q == jj ? reinterpret_cast<const u32x4 *>(&W.u.t.pbuf[2 * hf + (jj >> 1)][kc2][ah][wr][0])
+          const u32x4 *src = q == jj ? reinterpret_cast<const u32x4 *>(&W.u.t.pbuf[2 * hf + (jj >> 1)][kc2][(wr * 4 + ah) * 8])
                                      : &W.zero;
           vacc[hf] = mfma16(*src, value_operand(V.vw[hf][wr], kc2), vacc[hf]);
         }
@@ -712,42 +720,37 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
     float zs[kChunk4][2][2];                         // this wavefront's logits of the chunk
     float zl[2] = {-INFINITY, -INFINITY};            // and their maximum per head of the pair
 
-    // ---- pass 1: keys.  Four blocks are in flight in registers.  Block i is
-    // written to LDS buffer i & 1 once its loads have landed, published by one
-    // barrier, then worked on; the barrier of block i also tells every
-    // wavefront that block i - 1, which used the other buffer, has been worked
-    // on by all of them.
+    // ---- pass 1: keys.  Block i is written to LDS buffer i & 1 once its loads
+    // have landed and is published by a barrier.  The body for block i works
+    // out its logits and, in the same straight-line code, writes block i + 1 to
+    // the other buffer (so the matrix products of one block overlap the vector
+    // work of the next), issues the loads of block i + 3 into the registers
+    // block i + 1 came in, and ends with the barrier that publishes block i + 1
+    // and tells every wavefront that block i is done with.  Loads run two
+    // blocks ahead of their commit.  Blocks past the chunk are committed as
+    // zeros (their loads are empty) and never read.
     KStage4<D> S0, S1;
     kissue(S0, c_t0, 0 < nbc);
     kissue(S1, c_t0 + kBlock4, 1 < nbc);
+    kcommit(S0, sm.kb[0], c_t0);
+    kissue(S0, c_t0 + 2 * kBlock4, 2 < nbc);
+    block_barrier();
 #pragma unroll
     for (int i = 0; i < kChunk4; ++i) {
       if (i >= nbc) break;
-      KStage4<D> &S = (i & 1) ? S1 : S0;
       const int p0 = c_t0 + kBlock4 * i;
-      kcommit(S, sm.kb[i & 1], p0);
-      kissue(S, p0 + 2 * kBlock4, i + 2 < nbc);
-      block_barrier();
-      const int tile0 = p0 + kTile4 * wave;
-      if (tile0 < t_end) {
-        logits(sm.kb[i & 1], tile0, zs[i]);
-      } else {
-        zs[i][0][0] = zs[i][0][1] = zs[i][1][0] = zs[i][1][1] = -INFINITY;
-      }
+      // every tile is worked on: tokens past the end get -inf inside logits()
+      logits(sm.kb[i & 1], p0 + kTile4 * wave, zs[i]);
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) zl[hh] = fmaxf(zl[hh], fmaxf(zs[i][hh][0], zs[i][hh][1]));
-    }
-    float z9[2][2];   // the ninth block (stage S0 and LDS buffer 0, as block 8 of the loop would use)
-    if (nbc > kChunk4) {
-      const int p0 = c_t0 + kBlock4 * kChunk4;
-      kcommit(S0, sm.kb[0], p0);
+      KStage4<D> &S = (i & 1) ? S0 : S1;   // holds block i + 1
+      kcommit(S, sm.kb[(i + 1) & 1], p0 + kBlock4);
+      kissue(S, p0 + 3 * kBlock4, i + 3 < nbc);
       block_barrier();
-      const int tile0 = p0 + kTile4 * wave;
-      if (tile0 < t_end) {
-        logits(sm.kb[0], tile0, z9);
-      } else {
-        z9[0][0] = z9[0][1] = z9[1][0] = z9[1][1] = -INFINITY;
-      }
+    }
+    float z9[2][2];   // the ninth block: committed to buffer 0 by the body of block 8
+    if (nbc > kChunk4) {
+      logits(sm.kb[0], c_t0 + kBlock4 * kChunk4 + kTile4 * wave, z9);
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) zl[hh] = fmaxf(zl[hh], fmaxf(z9[hh][0], z9[hh][1]));
     }

@@ -16,18 +16,23 @@
 // Built with -ffp-contract=off.
 #include "dqk_internal.h"
 
+#include <type_traits>
+
 namespace dqk {
 namespace {
 
-constexpr int kThreads = 128;
+constexpr int kThreads = 256;
 
 __device__ __forceinline__ int popc(unsigned long long m) { return __popcll(m); }
 
 // Exact top-(k) of one head's |q'| over channels 1..D-1 inside one wavefront:
 // lane l holds channels l and l+64.  Magnitudes are non-negative floats, so
-// their bit patterns order like the values; a 31-step bitwise search finds the
-// k-th largest pattern T, channels above T are kept, and of the channels equal
-// to T the lowest indices are kept.  Writes idx[0..keep) ascending.
+// their bit patterns order like the values; a bitwise search from the top bit
+// finds the k-th largest pattern T, channels above T are kept, and of the
+// channels equal to T the lowest indices are kept.  The search stops early once
+// exactly k patterns are at or above the prefix found so far: that set is then
+// the answer (the full search would end on a T with the same set).  Writes
+// idx[0..keep) ascending.
 template <int D>
 __device__ void select_one_head(const float *mag, int keep, int32_t *idx) {
   const int lane = threadIdx.x & 63;
@@ -43,7 +48,10 @@ __device__ void select_one_head(const float *mag, int keep, int32_t *idx) {
     for (int bit = 30; bit >= 0; --bit) {
       const uint32_t cand = t | (1u << bit);
       const int n = popc(__ballot(v0 && k0 >= cand)) + popc(__ballot(v1 && k1 >= cand));
-      if (n >= want) t = cand;
+      if (n >= want) {
+        t = cand;
+        if (n == want) break;
+      }
     }
     const unsigned long long g0 = __ballot(v0 && k0 > t), g1 = __ballot(v1 && k1 > t);
     const unsigned long long e0 = __ballot(v0 && k0 == t), e1 = __ballot(v1 && k1 == t);
@@ -59,14 +67,15 @@ __device__ void select_one_head(const float *mag, int keep, int32_t *idx) {
 }
 
 // One workgroup per (batch row, KV head); the G query heads of the group share
-// every load of A_g.  Lane j forms q'_j of all G heads; each wavefront then
-// selects for every other head.
+// A_g.  Thread j forms q'_c for column c = j % D of the heads of its thread
+// group j / D (G heads spread over kThreads / D groups); each wavefront then
+// selects for every fourth head.
 template <int D, int G, bool BF16>
 __global__ __launch_bounds__(kThreads) void select_kernel(const void *q,
                                                           const float *__restrict__ amat, int hq,
                                                           int hkv, int keep, float *q_prime,
                                                           int32_t *sel_idx) {
-  __shared__ float qs[G][D];
+  __shared__ __attribute__((aligned(16))) float qs[G][D];
   __shared__ float mag[G][D];
   const int b = blockIdx.x / hkv, g = blockIdx.x % hkv;
   const size_t row0 = (size_t)b * hq + (size_t)g * G;
@@ -83,29 +92,52 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const void *q,
     else
       qv[k] = static_cast<const float *>(q)[row0 * D + e];
   }
+  constexpr int NGRP = kThreads / D;            // thread groups (one per D threads)
+  constexpr int HPT = (G + NGRP - 1) / NGRP;    // heads per thread
+  const int col = j % D, grp = j / D;           // grp is uniform in a wavefront
   float a[D];
-  const float *acol = amat + (size_t)g * D * D + (j < D ? j : 0);
+  const float *acol = amat + (size_t)g * D * D + col;
 #pragma unroll
   for (int r = 0; r < D; ++r) a[r] = acol[(size_t)r * D];
 #pragma unroll
-  for (int k = 0; k < QJ; ++k) {
-    const int e = j + kThreads * k;
-    if (e < G * D) qs[e / D][e % D] = qv[k];
+  for (int k = 0; k < QJ; ++k) {   // clamped like the loads: the last element may be written twice
+    const int e = min(j + kThreads * k, G * D - 1);
+    qs[e / D][e % D] = qv[k];
   }
-  __syncthreads();
-  if (j < D) {
-    float acc[G];
+  // A's column is used here so that its loads are issued before the barrier,
+  // together with the query loads (A is read-only: the compiler would otherwise
+  // move them past the barrier, a second round trip)
 #pragma unroll
-    for (int h = 0; h < G; ++h) acc[h] = 0.0f;
+  for (int r = 0; r < D; ++r) asm volatile("" ::"v"(a[r]));
+  __syncthreads();
+  // thread group GRP's heads as compile-time rows of qs (a runtime head index
+  // makes the compiler hoist every LDS read of the chain at once)
+  auto chain = [&](auto grp_c) {
+    constexpr int GRP = decltype(grp_c)::value;
+    float acc[HPT];
+#pragma unroll
+    for (int i = 0; i < HPT; ++i) acc[i] = 0.0f;
 #pragma unroll
     for (int r = 0; r < D; ++r)
 #pragma unroll
-      for (int h = 0; h < G; ++h) acc[h] = __builtin_fmaf(qs[h][r], a[r], acc[h]);
+      for (int i = 0; i < HPT; ++i) {
+        acc[i] = __builtin_fmaf(qs[min(GRP * HPT + i, G - 1)][r], a[r], acc[i]);
+      }
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      q_prime[(row0 + h) * D + j] = acc[h];
-      mag[h][j] = fabsf(acc[h]);
+    for (int i = 0; i < HPT; ++i) {
+      const int h = GRP * HPT + i;
+      if (h < G) {
+        q_prime[(row0 + h) * D + col] = acc[i];
+        mag[h][col] = fabsf(acc[i]);
+      }
     }
+  };
+  static_assert(NGRP <= 4, "thread groups");
+  switch (grp) {   // uniform in a wavefront
+    case 0: chain(std::integral_constant<int, 0>{}); break;
+    case 1: if constexpr (NGRP > 1) chain(std::integral_constant<int, 1>{}); break;
+    case 2: if constexpr (NGRP > 2) chain(std::integral_constant<int, 2>{}); break;
+    default: if constexpr (NGRP > 3) chain(std::integral_constant<int, 3>{}); break;
   }
   __syncthreads();
   for (int h = wave; h < G; h += kThreads / 64) select_one_head<D>(mag[h], keep, sel_idx + (row0 + h) * keep);
