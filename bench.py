@@ -212,6 +212,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--split", type=int, default=0)
+    ap.add_argument("--graph", action=argparse.BooleanOptionalAction, default=True,
+                    help="also time the steps captured as one HIP graph (the reported value)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after the timed steps, copy this many MiB device to device "
                          "(a known-size reference for HBM byte counters)")
@@ -267,8 +269,10 @@ def main():
     log(f"{args.copies} cache copies of {caches[0].nbytes() / 1e6:.1f} MB built")
 
     nstep = args.warmup + args.steps
-    step_kv = torch.randn((nstep, wl.batch, wl.hkv, 1, wl.d), device=dev).to(torch.bfloat16)
-    step_q = torch.stack([to_bf16(W.bf16_bits(W.queries(wl, i))) for i in range(nstep)])
+    # step inputs: the eager steps, then the steps captured in the graph (replayed twice)
+    ninputs = nstep + (args.steps if args.graph else 0)
+    step_kv = torch.randn((ninputs, wl.batch, wl.hkv, 1, wl.d), device=dev).to(torch.bfloat16)
+    step_q = torch.stack([to_bf16(W.bf16_bits(W.queries(wl, i))) for i in range(ninputs)])
     ones = torch.ones((wl.batch,), dtype=torch.int32, device=dev)
     qp = torch.empty((wl.batch, wl.hq, wl.d), dtype=torch.float32, device=dev)
     idx = torch.empty((wl.batch, wl.hq, keep), dtype=torch.int32, device=dev)
@@ -276,16 +280,21 @@ def main():
     ws = torch.empty(M.decode_workspace_bytes(caches[0], wl.hq, args.split), dtype=torch.uint8,
                      device=dev)
 
-    # algorithmic bytes of every step (selections are deterministic given q)
+    # algorithmic bytes of every step in the order the steps run (selections are
+    # deterministic given q; a step's bytes depend on its cache's length)
+    graph_idx = list(range(nstep, ninputs))
+    schedule = list(range(nstep)) + graph_idx + graph_idx   # eager, graph warm replay, timed replay
     lens = [np.full(wl.batch, ctx, dtype=np.int64) for _ in caches]
     step_bytes, dec_bytes = [], []
-    for i in range(nstep):
+    idx_of = {}
+    for i in schedule:
         ci = i % len(caches)
-        M.select_channels(step_q[i], a_d, wl.hkv, keep, qp, idx)
-        idx_np = idx.cpu().numpy()
+        if i not in idx_of:
+            M.select_channels(step_q[i], a_d, wl.hkv, keep, qp, idx)
+            idx_of[i] = idx.cpu().numpy()
         pos = lens[ci].copy()
         lens[ci] += 1
-        db = decode_bytes(idx_np, lens[ci], wl.hkv, wl.d, keep)
+        db = decode_bytes(idx_of[i], lens[ci], wl.hkv, wl.d, keep)
         dec_bytes.append(db)
         step_bytes.append(db + select_bytes(wl.batch, wl.hq, wl.hkv, wl.d, keep, 2)
                           + append_bytes(wl.batch, wl.hkv, wl.d, pos, 2))
@@ -321,6 +330,32 @@ def main():
     log(f"step {ms_step * 1e3:.1f} us, decode (partial+combine) {dec_avg_ms * 1e3:.1f} us "
         f"(p10 {np.percentile(dec_ms, 10) * 1e3:.1f} p90 {np.percentile(dec_ms, 90) * 1e3:.1f}), "
         f"append+select {np.mean(pre_ms) * 1e3:.1f} us, {gbs:.0f} GB/s step, {dec_gbs:.0f} GB/s decode")
+    eager = {"ms_per_step": round(ms_step, 5), "value": round(gbs, 2)}
+
+    if args.graph:
+        # The same step, K more times, captured once as a HIP graph (no host work per
+        # launch) and replayed: one untimed replay, then the timed one.
+        def step_plain(i):
+            c = caches[i % len(caches)]
+            M.transform_quantize_append(c, step_kv[i], step_kv[i], b_d, ones)
+            M.select_channels(step_q[i], a_d, wl.hkv, keep, qp, idx)
+            M.decode_attention(c, qp, idx, sm, args.split, out, ws)
+
+        graph = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            for i in graph_idx:
+                step_plain(i)
+        graph.replay()
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        graph.replay()
+        torch.cuda.synchronize()
+        gwall = time.perf_counter() - t_start
+        g_bytes = sum(step_bytes[len(schedule) - args.steps:])
+        ms_step = 1e3 * gwall / args.steps
+        gbs = g_bytes / gwall / 1e9
+        log(f"graph-replayed step {ms_step * 1e3:.1f} us, {gbs:.0f} GB/s step")
 
     if args.calibrate_copy_mib > 0:
         n = args.calibrate_copy_mib << 20
@@ -353,7 +388,10 @@ def main():
                                f"INT2 K/V groups of 32, {args.sparsity}% query-channel sparsity, "
                                "step = append 1 token + select + decode",
                    "global_batch": wl.batch, "seq_len": ctx, "parallelism": "none (1 GPU)",
-                   "keep": keep, "cache_copies": args.copies},
+                   "keep": keep, "cache_copies": args.copies,
+                   "timing": ("the K steps captured once as a HIP graph and replayed "
+                              "(untimed replay first); the eager loop is under 'eager'"
+                              if args.graph else "eager launches")},
         "tokens_per_s": round(wl.batch / (ms_step * 1e-3), 1),
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
@@ -361,6 +399,8 @@ def main():
                      "bytes_per_launch": int(np.mean([dec_bytes[i] for i in timed])),
                      "avg_us": round(dec_avg_ms * 1e3, 2)},
     }
+    if args.graph:
+        result["eager"] = eager
     if extras:
         result["extras"] = extras
     if not args.no_cpu_baseline:

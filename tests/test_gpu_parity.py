@@ -323,6 +323,53 @@ def test_decode_ctx128k_sampled(orc):
             assert err <= REL_TOL, (extra, g, err)
 
 
+def test_step_graph_replay_matches_eager(orc):
+    """The decode step (append one token, select, decode) captured as a HIP graph:
+    three replays, each followed by the same step run eagerly on a twin cache, with
+    synchronisations between; every replay's cache planes, q', indices and output
+    are bitwise those of the eager step.  No launch on the path records a memset."""
+    wl = W.workload("gqa8k", batch=2, ctx=2600)
+    ga, a, b, k, v = build_gpu(wl)
+    gb, _, _, _, _ = build_gpu(wl, kv=(k, v))
+    a_d, b_d = dev_f32(a), dev_f32(b)
+    keep = orc.keep_count(wl.d, 40)
+    sm = W.default_sm_scale(wl.d)
+    rng = np.random.default_rng(5)
+    kx = torch.from_numpy(rng.standard_normal((wl.batch, wl.hkv, 1, wl.d)).astype(np.float32)).to(
+        torch.bfloat16).cuda()
+    q = dev_input(W.queries(wl, 1), wl.dtype)
+    ones = torch.ones((wl.batch,), dtype=torch.int32, device="cuda")
+    qp = torch.empty((wl.batch, wl.hq, wl.d), dtype=torch.float32, device="cuda")
+    idx = torch.empty((wl.batch, wl.hq, keep), dtype=torch.int32, device="cuda")
+    out = torch.empty((wl.batch, wl.hq, wl.d), dtype=torch.float32, device="cuda")
+    ws = torch.empty(M.decode_workspace_bytes(ga, wl.hq, 0), dtype=torch.uint8, device="cuda")
+
+    def step(c, qp_, idx_, out_, ws_):
+        M.transform_quantize_append(c, kx, kx, b_d, ones)
+        M.select_channels(q, a_d, wl.hkv, keep, qp_, idx_)
+        M.decode_attention(c, qp_, idx_, sm, 0, out_, ws_)
+
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        step(ga, qp, idx, out, ws)
+    torch.cuda.synchronize()
+    for r in range(3):
+        say("graph replay", r)
+        graph.replay()
+        torch.cuda.synchronize()
+        qp_e, idx_e = torch.empty_like(qp), torch.empty_like(idx)
+        out_e, ws_e = torch.empty_like(out), torch.empty_like(ws)
+        step(gb, qp_e, idx_e, out_e, ws_e)
+        torch.cuda.synchronize()
+        pa, pb = planes_np(ga), planes_np(gb)
+        for name in pa:
+            assert np.array_equal(pa[name], pb[name]), (r, name)
+        assert np.array_equal(qp.cpu().numpy().view(np.uint32), qp_e.cpu().numpy().view(np.uint32))
+        assert np.array_equal(idx.cpu().numpy(), idx_e.cpu().numpy())
+        assert np.array_equal(out.cpu().numpy().view(np.uint32), out_e.cpu().numpy().view(np.uint32)), r
+
+
 def test_decode_poisoned_dropped_channels(orc):
     """Codes and scales of channels no head of the group keeps are overwritten
     with 0xFF / fp16 NaN: the output is bitwise unchanged, so they are never used."""
