@@ -305,8 +305,7 @@ def main():
         c = caches[i % len(caches)]
         e = ev[i]
         e[0].record()
-        M.transform_quantize_append(c, step_kv[i], step_kv[i], b_d, ones)
-        M.select_channels(step_q[i], a_d, wl.hkv, keep, qp, idx)
+        M.append_select(c, step_kv[i], step_kv[i], b_d, ones, step_q[i], a_d, keep, qp, idx)
         e[1].record()
         M.decode_attention(c, qp, idx, sm, args.split, out, ws)
         e[2].record()
@@ -337,8 +336,7 @@ def main():
         # launch) and replayed: one untimed replay, then the timed one.
         def step_plain(i):
             c = caches[i % len(caches)]
-            M.transform_quantize_append(c, step_kv[i], step_kv[i], b_d, ones)
-            M.select_channels(step_q[i], a_d, wl.hkv, keep, qp, idx)
+            M.append_select(c, step_kv[i], step_kv[i], b_d, ones, step_q[i], a_d, keep, qp, idx)
             M.decode_attention(c, qp, idx, sm, args.split, out, ws)
 
         graph = torch.cuda.CUDAGraph()

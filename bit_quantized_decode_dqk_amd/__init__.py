@@ -32,7 +32,8 @@ class _Cache(C.Structure):
 
 _lib = None
 EXPORTS = ("dqk_status_str", "dqk_cache_plane_bytes", "dqk_transform_quantize_append",
-           "dqk_select_channels", "dqk_decode_workspace_bytes", "dqk_decode_attention",
+           "dqk_select_channels", "dqk_append_select", "dqk_decode_workspace_bytes",
+           "dqk_decode_attention",
            "dqk_dequant_reference", "dqk_bf16_decode_workspace_bytes",
            "dqk_bf16_decode_attention", "dqk_debug_f16_from_f32")
 
@@ -52,6 +53,7 @@ def lib():
             "dqk_cache_plane_bytes": [I, I, I, I, P],
             "dqk_transform_quantize_append": [C.POINTER(_Cache), P, P, C.c_int, P, P, I, P],
             "dqk_select_channels": [P, C.c_int, P, I, I, I, I, I, P, P, P],
+            "dqk_append_select": [C.POINTER(_Cache), P, P, P, P, I, P, P, I, I, C.c_int, P, P, P],
             "dqk_decode_workspace_bytes": [C.POINTER(_Cache), I, I, P],
             "dqk_decode_attention": [C.POINTER(_Cache), P, P, I, I, C.c_float, I, P, P, S, P],
             "dqk_dequant_reference": [C.POINTER(_Cache), P, P, P],
@@ -174,6 +176,26 @@ def select_channels(q, amat, hkv: int, keep: int, q_prime=None, sel_idx=None, st
     _check(lib().dqk_select_channels(_ptr(q), _dtype_code(q), _ptr(amat), batch, hq, hkv, d, keep,
                                      _ptr(q_prime), _ptr(sel_idx), _stream(stream)),
            "dqk_select_channels")
+    return q_prime, sel_idx
+
+
+def append_select(cache: Cache, k_new, v_new, bmat, n_new, q, amat, keep: int, q_prime=None,
+                  sel_idx=None, stream=None):
+    """transform_quantize_append and select_channels of one step in one launch (q, k_new
+    and v_new of one dtype; the selection uses the cache's batch and KV heads)."""
+    torch = _torch()
+    if k_new.dtype != v_new.dtype or k_new.shape != v_new.shape or q.dtype != k_new.dtype:
+        raise DqkError("q, k_new and v_new must share a dtype; k_new and v_new a shape")
+    batch, hq, d = q.shape
+    if q_prime is None:
+        q_prime = torch.empty((batch, hq, d), dtype=torch.float32, device=q.device)
+    if sel_idx is None:
+        sel_idx = torch.empty((batch, hq, keep), dtype=torch.int32, device=q.device)
+    s = cache.struct()
+    _check(lib().dqk_append_select(C.byref(s), _ptr(k_new), _ptr(v_new), _ptr(bmat), _ptr(n_new),
+                                   int(k_new.shape[2]), _ptr(q), _ptr(amat), hq, keep,
+                                   _dtype_code(q), _ptr(q_prime), _ptr(sel_idx), _stream(stream)),
+           "dqk_append_select")
     return q_prime, sel_idx
 
 

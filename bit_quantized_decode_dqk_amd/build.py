@@ -25,6 +25,7 @@ SOURCES = {
     "dqk_api.cpp": ["-ffp-contract=off"],
     "dqk_append.hip": ["-ffp-contract=off"],
     "dqk_select.hip": ["-ffp-contract=off"],
+    "dqk_step.hip": ["-ffp-contract=off"],
     "dqk_dequant.hip": ["-ffp-contract=off"],
     "dqk_decode.hip": ["-fno-honor-nans"],   # inputs are finite; only -inf is used
     "dqk_decode4.hip": ["-fno-honor-nans"],

@@ -113,6 +113,30 @@ dqk_status dqk_select_channels(const void *q, dqk_dtype dtype, const float *amat
                                      sel_idx, reinterpret_cast<hipStream_t>(stream)));
 }
 
+dqk_status dqk_append_select(const dqk_cache *cache, const void *k_new, const void *v_new,
+                             const float *bmat, const int32_t *n_new, int32_t max_new,
+                             const void *q, const float *amat, int32_t hq, int32_t keep,
+                             dqk_dtype dtype, float *q_prime, int32_t *sel_idx,
+                             dqk_stream_t stream) {
+  dqk_status st = check_cache(cache);
+  if (st != DQK_OK) return st;
+  if (dtype != DQK_F32 && dtype != DQK_BF16) return DQK_ERR_INVALID;
+  if (!k_new || !v_new || !bmat || !n_new || max_new < 0) return DQK_ERR_INVALID;
+  if ((int64_t)max_new > cache->capacity) return DQK_ERR_INVALID;
+  if (!q || !amat || !q_prime || !sel_idx) return DQK_ERR_INVALID;
+  const int hkv = cache->num_kv_heads;
+  if (hq <= 0 || hq % hkv != 0) return DQK_ERR_INVALID;
+  if (!supported_group(hq, hkv)) return DQK_ERR_UNSUPPORTED;
+  if (keep < 1 || keep > cache->head_dim) return DQK_ERR_INVALID;
+  if ((int64_t)cache->batch * hq > (1 << 30)) return DQK_ERR_INVALID;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (max_new == 0)
+    return from_hip(dqk::launch_select(q, dtype == DQK_BF16, amat, cache->batch, hq, hkv,
+                                       cache->head_dim, keep, q_prime, sel_idx, s));
+  return from_hip(dqk::launch_append_select(*cache, k_new, v_new, dtype == DQK_BF16, bmat, n_new,
+                                            max_new, q, amat, hq, keep, q_prime, sel_idx, s));
+}
+
 dqk_status dqk_decode_workspace_bytes(const dqk_cache *cache, int32_t hq, int32_t split,
                                       size_t *out) {
   if (!out) return DQK_ERR_INVALID;

@@ -1,0 +1,201 @@
+// Append step (the body of one workgroup, shared by the append kernel and the
+// fused append + selection kernel): key transform, channel-0 protection, per-channel key groups,
+// per-token value groups, 2-bit packing -- fused in one kernel.
+//
+// Dual-QK (arXiv abstract; tech.dede.sh summary, "Paired transforms instead of
+// shared rotation" and "Throughput on SGLang"): new keys go through the key
+// transform k' = k B, keys and values are stored in 2 bits with an fp16 scale
+// per group of 32, and channel 0 of the key is protected (kept in fp16 here).
+//
+// One workgroup handles one 32-token key group of one (batch row, KV head):
+// the new tokens of that group are transformed (each output one fp32 FMA chain
+// over input channels in ascending order, so the result is reproducible bit for
+// bit), channel 0 goes to fp16, and either the group is complete -- then every
+// channel 1..d-1 is quantized over its 32 tokens and packed as 8 bytes -- or the
+// exact values go to the tail rows.  Value rows are quantized per token in
+// 32-channel groups; their codes are merged into the 16-token words of the
+// channel-blocked value plane.  Built with -ffp-contract=off.
+#pragma once
+#include "dqk_internal.h"
+
+namespace dqk {
+namespace appb {
+
+constexpr int kThreads = 256;
+
+template <int D>
+struct AppendSmem {
+  float kx[kGroup][D];   // new keys of the group (fp32)
+  float kp[kGroup][D];   // transformed keys
+  float vx[kGroup][D];   // new values (fp32)
+  float v2s[kGroup][D / kGroup];  // 2*scale per (token, value group)
+};
+
+template <bool BF16>
+__device__ __forceinline__ float load_in(const void *p, size_t i) {
+  if constexpr (BF16) return bf16_value(static_cast<const uint16_t *>(p)[i]);
+  else return static_cast<const float *>(p)[i];
+}
+
+// bcol: this thread's column j = tid % D of B_g, all D rows, loaded at kernel
+// start before anything waits (used by single-token appends; bulk appends
+// stream the rows of B from bmat).
+template <int D, bool BF16>
+__device__ __forceinline__ void store_group(const dqk_cache &c, int b, int g, int grp, int L, int n,
+                                            const void *k_new, const void *v_new,
+                                            const float (&bcol)[D], const float *__restrict__ bmat,
+                                            int max_new, AppendSmem<D> &sm) {
+  const int tid = threadIdx.x;
+  const int lo = max(L, grp * kGroup);
+  const int hi = min(L + n, grp * kGroup + kGroup);
+  const int cnt = hi - lo;                    // new tokens in this group, 1..32
+  const size_t unit = unit_index(c, b, g);
+  const size_t row0 = (unit * (size_t)max_new + (size_t)(lo - L)) * D;
+
+  // The group's value words (two 16-token words per channel, one per thread)
+  // are read now, in flight with the inputs, and rewritten at the end.
+  static_assert(2 * D <= kThreads, "one value word per thread");
+  const int vch = tid % D, vhalf = (tid / D) & 1;
+  const int wlo = grp * kGroup + vhalf * 16;
+  const int va = max(wlo, lo), vz = min(wlo + 16, hi);   // new tokens of this word: [va, vz)
+  uint32_t *wp = c.v_codes + (unit * (size_t)(c.capacity / 16) + (size_t)(wlo >> 4)) * D + vch;
+  const uint32_t wold = *wp;
+
+  // two elements of k and of v per thread in flight; the second index is
+  // clamped to the last element, which is then written twice with the same
+  // value (no branch, so no load waits behind another)
+  for (int e0 = tid; e0 < cnt * D; e0 += 2 * kThreads) {
+    const int e1 = min(e0 + kThreads, cnt * D - 1);
+    const float k0 = load_in<BF16>(k_new, row0 + e0), v0 = load_in<BF16>(v_new, row0 + e0);
+    const float k1 = load_in<BF16>(k_new, row0 + e1), v1 = load_in<BF16>(v_new, row0 + e1);
+    sm.kx[e0 / D][e0 % D] = k0;
+    sm.vx[e0 / D][e0 % D] = v0;
+    sm.kx[e1 / D][e1 % D] = k1;
+    sm.vx[e1 / D][e1 % D] = v1;
+  }
+  __syncthreads();
+
+  // k' = k B: thread owns output channel j for tokens r0, r0+S, ...
+  {
+    constexpr int S = kThreads / D;           // token slots per channel
+    constexpr int R = kGroup / S;             // tokens per thread at most
+    const int j = tid % D, r0 = tid / D;
+    if (cnt <= S) {                            // decode-step appends: one token per thread
+      float acc = 0.0f;
+#pragma unroll
+      for (int i = 0; i < D; ++i) acc = __builtin_fmaf(sm.kx[r0][i], bcol[i], acc);
+      if (r0 < cnt) sm.kp[r0][j] = acc;
+    } else {
+      // rows of B fetched kBRows at a time so that many loads are in flight
+      constexpr int kBRows = 16;
+      const float *bc = bmat + (size_t)g * D * D + j;
+      float acc[R];
+#pragma unroll
+      for (int m = 0; m < R; ++m) acc[m] = 0.0f;
+#pragma unroll 1
+      for (int i0 = 0; i0 < D; i0 += kBRows) {   // (a full unroll would spill)
+        float bv[kBRows];
+#pragma unroll
+        for (int r = 0; r < kBRows; ++r) bv[r] = bc[(size_t)(i0 + r) * D];
+#pragma unroll
+        for (int r = 0; r < kBRows; ++r)
+#pragma unroll
+          for (int m = 0; m < R; ++m)
+            acc[m] = __builtin_fmaf(sm.kx[r0 + m * S][i0 + r], bv[r], acc[m]);
+      }
+#pragma unroll
+      for (int m = 0; m < R; ++m)
+        if (r0 + m * S < cnt) sm.kp[r0 + m * S][j] = acc[m];
+    }
+  }
+  __syncthreads();
+
+  uint16_t *ch0 = c.k_ch0 + unit * (size_t)c.capacity;
+  for (int r = tid; r < cnt; r += kThreads) ch0[lo + r] = f16_bits(sm.kp[r][0]);
+
+  if (hi == grp * kGroup + kGroup) {
+    // The group is complete: quantize channels 1..D-1 over its 32 tokens.
+    const float *tail = c.k_tail + unit * (size_t)kGroup * D;
+    for (int ch = 1 + tid; ch < D; ch += kThreads) {
+      float x[kGroup];
+      float mx = 0.0f;
+#pragma unroll
+      for (int r = 0; r < kGroup; ++r) {
+        const int p = grp * kGroup + r;
+        x[r] = p < lo ? tail[(size_t)r * D + ch] : sm.kp[p - lo][ch];
+        mx = fmaxf(mx, fabsf(x[r]));
+      }
+      const uint16_t sb = f16_bits(mx / 3.0f);
+      const float two_s = 2.0f * f16_value(sb);
+      uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        w0 |= code_of(x[r], two_s) << (2 * r);
+        w1 |= code_of(x[r + 16], two_s) << (2 * r);
+      }
+      uint8_t *row = c.k_codes + (unit * D + ch) * (size_t)(c.capacity / 4);
+      *reinterpret_cast<uint2 *>(row + (size_t)grp * 8) = make_uint2(w0, w1);
+      c.k_scales[(unit * D + ch) * (size_t)(c.capacity / kGroup) + grp] = sb;
+    }
+  } else {
+    float *tail = c.k_tail + unit * (size_t)kGroup * D;
+    for (int e = tid; e < cnt * D; e += kThreads)
+      tail[(size_t)((lo + e / D) & 31) * D + e % D] = sm.kp[e / D][e % D];
+  }
+
+  // Value scales: one per (new token, 32-channel group).
+  constexpr int VG = D / kGroup;
+  uint16_t *vsc = c.v_scales + unit * (size_t)c.capacity * VG;
+  for (int e = tid; e < cnt * VG; e += kThreads) {
+    const int r = e / VG, jg = e % VG;
+    float mx = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i) mx = fmaxf(mx, fabsf(sm.vx[r][jg * kGroup + i]));
+    const uint16_t sb = f16_bits(mx / 3.0f);
+    vsc[(size_t)(lo + r) * VG + jg] = sb;
+    sm.v2s[r][jg] = 2.0f * f16_value(sb);
+  }
+  __syncthreads();
+
+  // Value codes: merge the new tokens' codes into the word read at the start
+  // (a word without new tokens is written back unchanged).
+  uint32_t w = wold;
+  for (int p = va; p < vz; ++p) {
+    const int sh = 2 * (p & 15);
+    const uint32_t u = code_of(sm.vx[p - lo][vch], sm.v2s[p - lo][vch / kGroup]);
+    w = (w & ~(3u << sh)) | (u << sh);
+  }
+  if (tid < 2 * D) *wp = w;
+  __syncthreads();
+}
+
+template <int D, bool BF16>
+__device__ __forceinline__ void append_block(int block, const dqk_cache &c, const void *k_new,
+                                             const void *v_new, const float *__restrict__ bmat,
+                                             const int32_t *__restrict__ n_new, int max_new,
+                                             int blocks_per_unit) {
+  __shared__ AppendSmem<D> sm;
+  const int unit = block / blocks_per_unit;
+  const int bi = block % blocks_per_unit;
+  const int b = unit / c.num_kv_heads, g = unit % c.num_kv_heads;
+  // column tid % D of B_g, in flight together with the length
+  float bcol[D];
+  const float *bp = bmat + (size_t)g * D * D + threadIdx.x % D;
+#pragma unroll
+  for (int i = 0; i < D; ++i) bcol[i] = bp[(size_t)i * D];
+  const int L = c.lengths[b];
+  const int n = max(0, min(min(n_new[b], max_new), c.capacity - L));
+  if (n <= 0) return;
+  const int g0 = L / kGroup, g1 = (L + n - 1) / kGroup;
+  // The first group may read old tail rows while the last (unfinished) group
+  // writes tail rows; then one workgroup does both, first before last.
+  const bool merged = g1 > g0 && (L % kGroup) != 0 && ((L + n) % kGroup) != 0;
+  const int ngroups = g1 - g0 + 1;
+  if (bi >= ngroups) return;
+  if (merged && bi == ngroups - 1) return;
+  store_group<D, BF16>(c, b, g, g0 + bi, L, n, k_new, v_new, bcol, bmat, max_new, sm);
+  if (merged && bi == 0) store_group<D, BF16>(c, b, g, g1, L, n, k_new, v_new, bcol, bmat, max_new, sm);
+}
+
+}  // namespace appb
+}  // namespace dqk

@@ -114,6 +114,21 @@ dqk_status dqk_select_channels(const void *q, dqk_dtype dtype, const float *amat
                                int32_t keep, float *q_prime, int32_t *sel_idx,
                                dqk_stream_t stream);
 
+/* The append and the channel selection of one decode step in one launch: the
+ * new token's keys and values and its query are all inputs of the step, and the
+ * two parts share no data (tech.dede.sh summary, "Paired transforms instead of
+ * shared rotation": keys and queries each pass through their own transform).
+ * Same arguments, results and errors as dqk_transform_quantize_append followed
+ * by dqk_select_channels, except: q, k_new and v_new share `dtype`; the
+ * selection's batch and KV-head count are the cache's; hq / num_kv_heads in
+ * {1, 2, 4, 8}.  Launches two kernels (append and selection together, then
+ * lengths).  With max_new == 0 only the selection runs. */
+dqk_status dqk_append_select(const dqk_cache *cache, const void *k_new, const void *v_new,
+                             const float *bmat, const int32_t *n_new, int32_t max_new,
+                             const void *q, const float *amat, int32_t hq, int32_t keep,
+                             dqk_dtype dtype, float *q_prime, int32_t *sel_idx,
+                             dqk_stream_t stream);
+
 /* Host query: workspace bytes dqk_decode_attention needs for this cache shape,
  * hq query heads and split length (split_tokens = 0: the library's choice). */
 dqk_status dqk_decode_workspace_bytes(const dqk_cache *cache, int32_t hq,

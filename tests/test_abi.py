@@ -141,6 +141,36 @@ def test_append_select_dequant_validation_without_gpu():
     assert L.dqk_dequant_reference(C.byref(fake_cache(capacity=0)), 0x10, 0x20, None) == INVALID
 
 
+def test_fused_append_select_validation_without_gpu():
+    """dqk_append_select rejects what either of its two parts rejects (fake cache:
+    batch 2, 2 KV heads, head_dim 128, capacity 256)."""
+    L = M.lib()
+    c = C.byref(fake_cache())
+    k, v, b, n = 0x20000, 0x30000, 0x40000, 0x50000
+    q, a, qp, idx = 0x60000, 0x70000, 0x80000, 0x90000
+
+    def call(cache=c, k=k, v=v, b=b, n=n, max_new=1, q=q, a=a, hq=8, keep=77, dtype=1, qp=qp,
+             idx=idx):
+        return L.dqk_append_select(cache, k, v, b, n, max_new, q, a, hq, keep, dtype, qp, idx, None)
+
+    assert call(k=None) == INVALID
+    assert call(n=None) == INVALID
+    assert call(max_new=-1) == INVALID
+    assert call(max_new=257) == INVALID
+    assert call(dtype=7) == INVALID
+    assert call(q=None) == INVALID
+    assert call(a=None) == INVALID
+    assert call(idx=None) == INVALID
+    assert call(hq=0) == INVALID
+    assert call(hq=7) == INVALID          # not a multiple of the KV heads
+    assert call(hq=6) == UNSUPPORTED      # group of 3
+    assert call(keep=0) == INVALID
+    assert call(keep=129) == INVALID
+    assert call(cache=C.byref(fake_cache(head_dim=256))) == UNSUPPORTED
+    assert call(cache=C.byref(fake_cache(capacity=100))) == INVALID
+    assert call(cache=None) == INVALID
+
+
 def test_bf16_decode_validation_without_gpu():
     L = M.lib()
     out = C.c_size_t(0)

@@ -138,6 +138,35 @@ def test_select_matches_oracle(orc, name):
         assert np.array_equal(idx.cpu().numpy(), idxo), keep
 
 
+@pytest.mark.parametrize("name,steps", [("tiny", (1, 1, 33)), ("gqa8k", (1, 40)), ("ragged64k", (1,))])
+def test_fused_append_select_matches_separate_calls(orc, name, steps):
+    """dqk_append_select against dqk_transform_quantize_append then
+    dqk_select_channels on a twin cache: planes, q' and indices bitwise equal,
+    for single-token and multi-token appends (a group flush and a straddle)."""
+    kw = dict(batch=2, ctx=700 if name == "gqa8k" else 900) if name != "tiny" else {}
+    wl = W.workload(name, steps=64, **kw)   # room for the appended tokens
+    g1, a, b, k, v = build_gpu(wl)
+    g2, _, _, _, _ = build_gpu(wl, kv=(k, v))
+    a_d, b_d = dev_f32(a), dev_f32(b)
+    keep = orc.keep_count(wl.d, 40)
+    rng = np.random.default_rng(9)
+    for st, n in enumerate(steps):
+        say(f"fused append+select {name}: {n} token(s)")
+        x = rng.standard_normal((wl.batch, wl.hkv, n, wl.d)).astype(np.float32)
+        kx = dev_f32(x) if wl.dtype == "f32" else torch.from_numpy(x).to(torch.bfloat16).cuda()
+        q = dev_input(W.queries(wl, 2 + st), wl.dtype)
+        counts = dev_i32(np.full(wl.batch, n, dtype=np.int32))
+        qp1, idx1 = M.append_select(g1, kx, kx, b_d, counts, q, a_d, keep)
+        M.transform_quantize_append(g2, kx, kx, b_d, counts)
+        qp2, idx2 = M.select_channels(q, a_d, wl.hkv, keep)
+        torch.cuda.synchronize()
+        p1, p2 = planes_np(g1), planes_np(g2)
+        for nm in p1:
+            assert np.array_equal(p1[nm], p2[nm]), (n, nm)
+        assert np.array_equal(qp1.cpu().numpy().view(np.uint32), qp2.cpu().numpy().view(np.uint32))
+        assert np.array_equal(idx1.cpu().numpy(), idx2.cpu().numpy())
+
+
 def test_select_forced_ties(orc):
     """Duplicated, negated and signed-zero query channels: ties go to lower index."""
     d, hq = 128, 8
