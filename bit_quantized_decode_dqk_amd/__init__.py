@@ -134,7 +134,7 @@ class Cache:
             "k_tail": ((batch, hkv, GROUP, d), torch.float32),
             "v_codes": ((batch, hkv, cap // 16, d), torch.int32),        # 32-bit code words
             "v_scales": ((batch, hkv, cap, d // GROUP), torch.int16),    # fp16 bits
-            "lengths": ((batch,), torch.int32),
+            "lengths": ((2 * batch,), torch.int32),   # lengths, then arrival counters
         }
         for (name, (shape, dt)), nbytes in zip(shapes.items(), sizes):
             t = torch.zeros(shape, dtype=dt, device=device)

@@ -82,7 +82,7 @@ dqk_status dqk_cache_plane_bytes(int32_t batch, int32_t hkv, int32_t d, int32_t 
   out[3] = u * kGroup * d * 4;                  // k_tail
   out[4] = u * (cap / 16) * d * 4;              // v_codes
   out[5] = u * cap * (d / kGroup) * 2;          // v_scales
-  out[6] = (size_t)batch * 4;                   // lengths
+  out[6] = (size_t)batch * 8;                   // lengths, then the append's arrival counters
   return DQK_OK;
 }
 

@@ -1,5 +1,5 @@
-// Append step kernels (the workgroup body is in dqk_append_body.h), the length
-// commit, and the fp16 conversion hook.  Built with -ffp-contract=off.
+// Append step kernel (the workgroup body, with the length commit, is in
+// dqk_append_body.h) and the fp16 conversion hook.  Built with -ffp-contract=off.
 #include "dqk_append_body.h"
 
 namespace dqk {
@@ -14,15 +14,6 @@ __global__ __launch_bounds__(kThreads) void append_kernel(dqk_cache c, const voi
                                                           const int32_t *__restrict__ n_new,
                                                           int max_new, int blocks_per_unit) {
   appb::append_block<D, BF16>(blockIdx.x, c, k_new, v_new, bmat, n_new, max_new, blocks_per_unit);
-}
-
-__global__ void commit_lengths_kernel(int32_t *lengths, const int32_t *n_new, int batch,
-                                      int max_new, int cap) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= batch) return;
-  const int L = lengths[b];
-  const int n = max(0, min(min(n_new[b], max_new), cap - L));
-  lengths[b] = L + n;
 }
 
 __global__ void f16_convert_kernel(const float *x, uint16_t *out, size_t n) {
@@ -52,15 +43,6 @@ hipError_t launch_append(const dqk_cache &c, const void *k_new, const void *v_ne
       hipLaunchKernelGGL((append_kernel<128, false>), grid, dim3(kThreads), 0, s, c, k_new, v_new, bmat,
                          n_new, max_new, per_unit);
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_commit_lengths(c, n_new, max_new, s);
-}
-
-hipError_t launch_commit_lengths(const dqk_cache &c, const int32_t *n_new, int max_new,
-                                 hipStream_t s) {
-  hipLaunchKernelGGL(commit_lengths_kernel, dim3((c.batch + 255) / 256), dim3(256), 0, s,
-                     c.lengths, n_new, c.batch, max_new, c.capacity);
   return hipGetLastError();
 }
 

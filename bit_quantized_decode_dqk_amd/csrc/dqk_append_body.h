@@ -191,10 +191,19 @@ __device__ __forceinline__ void append_block(int block, const dqk_cache &c, cons
   // writes tail rows; then one workgroup does both, first before last.
   const bool merged = g1 > g0 && (L % kGroup) != 0 && ((L + n) % kGroup) != 0;
   const int ngroups = g1 - g0 + 1;
-  if (bi >= ngroups) return;
-  if (merged && bi == ngroups - 1) return;
-  store_group<D, BF16>(c, b, g, g0 + bi, L, n, k_new, v_new, bcol, bmat, max_new, sm);
-  if (merged && bi == 0) store_group<D, BF16>(c, b, g, g1, L, n, k_new, v_new, bcol, bmat, max_new, sm);
+  if (bi < ngroups && !(merged && bi == ngroups - 1)) {
+    store_group<D, BF16>(c, b, g, g0 + bi, L, n, k_new, v_new, bcol, bmat, max_new, sm);
+    if (merged && bi == 0) store_group<D, BF16>(c, b, g, g1, L, n, k_new, v_new, bcol, bmat, max_new, sm);
+  }
+  // Length commit: every workgroup of the row (with or without a group to store)
+  // counts itself in on the row's arrival counter after it has read the length;
+  // the last of the row's num_kv_heads * blocks_per_unit workgroups writes the
+  // new length, and the counter wraps back to zero for the next append.
+  if (threadIdx.x == 0) {
+    const unsigned total = (unsigned)(c.num_kv_heads * blocks_per_unit);
+    unsigned *arrivals = reinterpret_cast<unsigned *>(c.lengths + c.batch);
+    if (atomicInc(&arrivals[b], total - 1) == total - 1) c.lengths[b] = L + n;
+  }
 }
 
 }  // namespace appb

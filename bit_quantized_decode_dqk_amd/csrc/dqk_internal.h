@@ -73,10 +73,7 @@ hipError_t launch_append(const dqk_cache &c, const void *k_new, const void *v_ne
                          const float *bmat, const int32_t *n_new, int max_new, hipStream_t s);
 hipError_t launch_select(const void *q, bool bf16, const float *amat, int batch, int hq, int hkv,
                          int d, int keep, float *q_prime, int32_t *sel_idx, hipStream_t s);
-// lengths[b] += n (the append's last launch)
-hipError_t launch_commit_lengths(const dqk_cache &c, const int32_t *n_new, int max_new,
-                                 hipStream_t s);
-// the append and the selection of one step in one launch (then the length commit);
+// the append and the selection of one step in one launch;
 // q, k_new and v_new share one dtype, the selection's batch and KV heads are the cache's
 hipError_t launch_append_select(const dqk_cache &c, const void *k_new, const void *v_new,
                                 bool bf16, const float *bmat, const int32_t *n_new, int max_new,

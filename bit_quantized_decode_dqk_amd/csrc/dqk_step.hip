@@ -4,7 +4,7 @@
 // their own transforms; arXiv abstract -- INT2 cache, dynamic channel pruning).
 // The selection workgroups (one per (row, KV head); they take longer) come first
 // in the grid, the append workgroups after them; each runs the same body as in
-// its own kernel.  The length commit follows as its own launch.  Built with
+// its own kernel (the append workgroups commit the lengths).  Built with
 // -ffp-contract=off.
 #include "dqk_append_body.h"
 #include "dqk_select_body.h"
@@ -68,8 +68,7 @@ hipError_t launch_append_select(const dqk_cache &c, const void *k_new, const voi
       c.head_dim == 64
           ? launch_d<64>(c, k_new, v_new, bf16, bmat, n_new, max_new, q, amat, hq, keep, q_prime, sel_idx, s)
           : launch_d<128>(c, k_new, v_new, bf16, bmat, n_new, max_new, q, amat, hq, keep, q_prime, sel_idx, s);
-  if (e != hipSuccess) return e;
-  return launch_commit_lengths(c, n_new, max_new, s);
+  return e;
 }
 
 }  // namespace dqk

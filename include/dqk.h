@@ -22,7 +22,7 @@
  *    contents of lengths/n_new/sel_idx, non-finite data) are preconditions; the
  *    kernels clamp counts and indices so they never write out of bounds.
  *
- * Cache layout, version 1 (per batch row b and KV head g, "unit" = b*hkv + g):
+ * Cache layout, version 2 (per batch row b and KV head g, "unit" = b*hkv + g):
  *   k_codes  u8   [batch][hkv][d][cap/4]   key channel c, token t: byte t>>2 of the
  *                                          channel's row, bits 2(t&3) (channel-major,
  *                                          so a dropped channel is never read)
@@ -33,10 +33,14 @@
  *   v_codes  u32  [batch][hkv][cap/16][d]  value token t, channel c: 32-bit word
  *                                          (t>>4)*d + c, bits 2(t&15)
  *   v_scales f16  [batch][hkv][cap][d/32]  scale of (token t, channels 32j..32j+31)
- *   lengths  i32  [batch]                  tokens stored per row
+ *   lengths  i32  [2][batch]               tokens stored per row, then one
+ *                                          arrival counter per row that the append
+ *                                          uses to commit the lengths (zero before
+ *                                          and after every append)
  * A 2-bit code u with scale s stands for s*(2u-3).  Rows of channel 0 in
- * k_codes/k_scales exist but are never written or read.  Planes should be
- * zero-filled before the first append for byte-reproducible contents.
+ * k_codes/k_scales exist but are never written or read.  All planes must be
+ * zero-filled before the first append (the counters must start at zero; the
+ * other planes then have byte-reproducible contents).
  */
 #ifndef DQK_H
 #define DQK_H
@@ -94,7 +98,8 @@ dqk_status dqk_cache_plane_bytes(int32_t batch, int32_t num_kv_heads, int32_t he
  *   quantized in groups of 32 channels.  Quantizer: s = fp16(max|x|/3),
  *   u = [x >= -2s] + [x >= 0] + [x >= 2s].
  * k_new, v_new: [batch][hkv][max_new][head_dim] of `dtype`; bmat: [hkv][d][d] fp32
- * row-major; n_new: [batch] i32.  Launches two kernels (store, then lengths). */
+ * row-major; n_new: [batch] i32.  One kernel: the last of a row's workgroups to
+ * finish writes the row's new length. */
 dqk_status dqk_transform_quantize_append(const dqk_cache *cache, const void *k_new,
                                          const void *v_new, dqk_dtype dtype,
                                          const float *bmat, const int32_t *n_new,
@@ -121,8 +126,7 @@ dqk_status dqk_select_channels(const void *q, dqk_dtype dtype, const float *amat
  * Same arguments, results and errors as dqk_transform_quantize_append followed
  * by dqk_select_channels, except: q, k_new and v_new share `dtype`; the
  * selection's batch and KV-head count are the cache's; hq / num_kv_heads in
- * {1, 2, 4, 8}.  Launches two kernels (append and selection together, then
- * lengths).  With max_new == 0 only the selection runs. */
+ * {1, 2, 4, 8}.  One kernel.  With max_new == 0 only the selection runs. */
 dqk_status dqk_append_select(const dqk_cache *cache, const void *k_new, const void *v_new,
                              const float *bmat, const int32_t *n_new, int32_t max_new,
                              const void *q, const float *amat, int32_t hq, int32_t keep,

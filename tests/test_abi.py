@@ -40,7 +40,7 @@ def test_status_strings():
 def test_plane_bytes():
     assert M.cache_plane_bytes(1, 8, 128, 131104) == [
         8 * 128 * 131104 // 4, 8 * 128 * (131104 // 32) * 2, 8 * 131104 * 2, 8 * 32 * 128 * 4,
-        8 * (131104 // 16) * 128 * 4, 8 * 131104 * 4 * 2, 4]
+        8 * (131104 // 16) * 128 * 4, 8 * 131104 * 4 * 2, 8]   # lengths + arrival counters
     out = (C.c_size_t * 7)()
     L = M.lib()
     assert L.dqk_cache_plane_bytes(1, 1, 96, 64, out) == UNSUPPORTED

@@ -163,6 +163,7 @@ def test_fused_append_select_matches_separate_calls(orc, name, steps):
         p1, p2 = planes_np(g1), planes_np(g2)
         for nm in p1:
             assert np.array_equal(p1[nm], p2[nm]), (n, nm)
+        assert not p1["lengths"][wl.batch:].any()   # arrival counters back at zero
         assert np.array_equal(qp1.cpu().numpy().view(np.uint32), qp2.cpu().numpy().view(np.uint32))
         assert np.array_equal(idx1.cpu().numpy(), idx2.cpu().numpy())
 
