@@ -332,14 +332,6 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
   __syncthreads();
   const int nu = sm.wcount[0] + sm.wcount[1];
   const int nkc = (nu + 15) / 16;
-  for (int e = tid; e < G * D; e += kThreads4) {
-    const int h = e / D, i = e % D;
-    const float mx = D > 64 ? fmaxf(sm.redm[h][0], sm.redm[h][1]) : sm.redm[h][0];
-    int ex = 0;
-    if (mx > 0.0f) frexpf(mx, &ex);
-    sm.coefs[h][i] = i < nu ? sm.coefc[h][sm.ulist[i]] * ldexpf(1.0f, -ex) : 0.0f;
-    if (i == 0) sm.e2[h] = ldexpf(1.0f, ex);
-  }
   // Tokens of the unfinished last key group (only in the workgroup that reaches
   // it): exact logits from the fp32 tail keys, one per (head, token).
   // The tail rows are staged in LDS first (the key block buffers are free until
@@ -377,7 +369,6 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
     }
   }
   __syncthreads();
-
   // Loads go through buffer resources of the unit's planes whose base is moved
   // to the block or tile (scalar arithmetic; the per-lane offsets stay fixed):
   // an offset past the resource returns zero, so absent parts point past the
@@ -413,12 +404,6 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
   uint32_t ksv[2];
   ksv[0] = as0 < nu ? (uint32_t)(sm.ulist[as0] * ks_stride * 2) + 4u * agp : kFar;
   ksv[1] = as1 < nu ? (uint32_t)(sm.ulist[as1] * ks_stride * 2) + 4u * agp : kFar;
-  float ca[G], cb[G];   // coefficients of the two slots per head (0 past |U|)
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    ca[h] = sm.coefs[h][as0];
-    cb[h] = sm.coefs[h][as1];
-  }
   // channel 0: dword tid (tokens 2 tid, 2 tid + 1) for the lower 128 lanes
   const uint32_t c0o = tid < kBlock4 / 2 ? 4u * tid : kFar;
 
@@ -440,6 +425,29 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
     // than the next block's for the partial waits to apply
     __builtin_amdgcn_sched_barrier(0);
   };
+
+  // The first chunk's first two blocks are issued now, before the coefficients are
+  // worked out: their latency overlaps the rest of the
+  // setup.
+  const int nbc0 = nb == kChunk4 + 1 ? kChunk4 + 1 : min(kChunk4, nb);
+  KStage4<D> S0, S1;
+  kissue(S0, t_begin, 0 < nbc0);
+  kissue(S1, t_begin + kBlock4, 1 < nbc0);
+  for (int e = tid; e < G * D; e += kThreads4) {
+    const int h = e / D, i = e % D;
+    const float mx = D > 64 ? fmaxf(sm.redm[h][0], sm.redm[h][1]) : sm.redm[h][0];
+    int ex = 0;
+    if (mx > 0.0f) frexpf(mx, &ex);
+    sm.coefs[h][i] = i < nu ? sm.coefc[h][sm.ulist[i]] * ldexpf(1.0f, -ex) : 0.0f;
+    if (i == 0) sm.e2[h] = ldexpf(1.0f, ex);
+  }
+  block_barrier();   // (not __syncthreads, which would wait for the loads just issued)
+  float ca[G], cb[G];   // coefficients of the two slots per head (0 past |U|)
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    ca[h] = sm.coefs[h][as0];
+    cb[h] = sm.coefs[h][as1];
+  }
 
   auto kcommit = [&](KStage4<D> &S, KBlock4<D> &B, int p0) {
     {
@@ -729,9 +737,10 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
     // and tells every wavefront that block i is done with.  Loads run two
     // blocks ahead of their commit.  Blocks past the chunk are committed as
     // zeros (their loads are empty) and never read.
-    KStage4<D> S0, S1;
-    kissue(S0, c_t0, 0 < nbc);
-    kissue(S1, c_t0 + kBlock4, 1 < nbc);
+    if (cb > 0) {   // the first chunk's were issued during the setup
+      kissue(S0, c_t0, 0 < nbc);
+      kissue(S1, c_t0 + kBlock4, 1 < nbc);
+    }
     kcommit(S0, sm.kb[0], c_t0);
     kissue(S0, c_t0 + 2 * kBlock4, 2 < nbc);
     block_barrier();
