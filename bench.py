@@ -377,6 +377,7 @@ def main():
     if not args.no_extras:
         extras = run_extras(M, torch, wl, caches, a_d, step_q, qp, idx, out, ws, k_d, v_d, sm,
                             args, roof_us)
+        extras["other_workloads"] = run_configs(M, torch)
 
     result = {
         "metric": "decode attention effective HBM GB/s + tokens/s at 128K ctx, INT2, 40% sparsity",
@@ -472,6 +473,112 @@ def run_extras(M, torch, wl, caches, a_d, step_q, qp, idx, out, ws, k_d, v_d, sm
     del k2, v2
     return res
 
+
+
+def run_configs(M, torch, steps: int = 32):
+    """The other workloads, one step each as on the 128K line: select + decode (the
+    tiny G = 1 case, GQA 32/8 at 8K, the ragged batch of 16 with G = 8) or the fused
+    append-1 + select, then decode (the 32K append loop, 64 steps).  Queries follow
+    each workload's recipe; the prefill K/V are drawn on the GPU from the same
+    distributions (timing does not depend on their values).  Cache copies rotate so
+    that at least 512 MB is streamed between visits to one copy.  Each is timed as a
+    captured HIP graph of its steps, replayed once untimed and once timed."""
+    dev = "cuda"
+    res = {}
+    for name in ("tiny", "gqa8k", "append32k", "ragged64k"):
+        t0 = time.time()
+        wl = W.workload(name)
+        appends = wl.steps > 0
+        n = wl.steps if appends else steps
+        keep = M.keep_for_sparsity(wl.d, wl.sparsity[0])
+        sm = W.default_sm_scale(wl.d)
+        # room for the eager warmup step and the two replays' appends
+        cap = W._cap_for(max(wl.ctx) + (2 * n + 8 if appends else 0))
+        cap = (cap + 63) // 64 * 64
+        a, b = W.transforms(wl)
+        a_d, b_d = torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev)
+        kscale = torch.from_numpy(W.key_scales(wl)).to(dev)
+        fdt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(1000 + wl.cid)
+        ctx_np = np.array(wl.ctx, dtype=np.int64)
+        cache0 = M.Cache(wl.batch, wl.hkv, wl.d, cap)
+        chunk = min(8192, cap)
+        for pos in range(0, int(ctx_np.max()), chunk):   # bounded staging memory
+            nn = np.clip(ctx_np - pos, 0, chunk)
+            k = torch.randn((wl.batch, wl.hkv, chunk, wl.d), generator=gen, device=dev)
+            k *= kscale[None, :, None, :]
+            v = torch.randn((wl.batch, wl.hkv, chunk, wl.d), generator=gen, device=dev)
+            v[..., 0] *= 8.0
+            M.transform_quantize_append(cache0, k.to(fdt), v.to(fdt), b_d,
+                                        torch.from_numpy(nn.astype(np.int32)).to(dev))
+            del k, v
+        torch.cuda.synchronize()
+        ncopy = int(min(16, max(1, -(-512_000_000 // cache0.nbytes()))))
+        caches = [cache0] + [M.Cache(wl.batch, wl.hkv, wl.d, cap) for _ in range(ncopy - 1)]
+        for c in caches[1:]:
+            for pname, t in cache0.planes().items():
+                getattr(c, pname).copy_(t)
+        qs = torch.stack([torch.from_numpy(W.queries(wl, i)).to(dev).to(fdt)
+                          for i in range(n + 1)])
+        kv = torch.randn((n + 1, wl.batch, wl.hkv, 1, wl.d), generator=gen, device=dev).to(fdt)
+        ones = torch.ones((wl.batch,), dtype=torch.int32, device=dev)
+        qp = torch.empty((wl.batch, wl.hq, wl.d), dtype=torch.float32, device=dev)
+        idx = torch.empty((wl.batch, wl.hq, keep), dtype=torch.int32, device=dev)
+        out = torch.empty((wl.batch, wl.hq, wl.d), dtype=torch.float32, device=dev)
+        ws = torch.empty(M.decode_workspace_bytes(cache0, wl.hq), dtype=torch.uint8, device=dev)
+
+        # algorithmic bytes of the timed replay (steps 1..n), lengths as they will be
+        lengths = [np.array(wl.ctx, dtype=np.int64) for _ in caches]
+        inb = 4 if wl.dtype == "f32" else 2
+
+        def advance(i):
+            ci = i % len(caches)
+            M.select_channels(qs[i], a_d, wl.hkv, keep, qp, idx)
+            nb = select_bytes(wl.batch, wl.hq, wl.hkv, wl.d, keep, inb)
+            if appends:
+                nb += append_bytes(wl.batch, wl.hkv, wl.d, lengths[ci], inb)
+                lengths[ci] = lengths[ci] + 1
+            return nb + decode_bytes(idx.cpu().numpy(), lengths[ci], wl.hkv, wl.d, keep)
+
+        def step(i):
+            c = caches[i % len(caches)]
+            if appends:
+                M.append_select(c, kv[i], kv[i], b_d, ones, qs[i], a_d, keep, qp, idx)
+            else:
+                M.select_channels(qs[i], a_d, wl.hkv, keep, qp, idx)
+            M.decode_attention(c, qp, idx, sm, 0, out, ws)
+
+        step(0)                                   # eager warmup (appends to copy 0)
+        torch.cuda.synchronize()
+        if appends:
+            lengths[0] = lengths[0] + 1
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(1, n + 1):
+                step(i)
+        graph.replay()                            # untimed replay
+        torch.cuda.synchronize()
+        for i in range(1, n + 1):                 # lengths after the untimed replay
+            if appends:
+                lengths[i % len(caches)] = lengths[i % len(caches)] + 1
+        tot = sum(advance(i) for i in range(1, n + 1))
+        torch.cuda.synchronize()
+        ts = time.perf_counter()
+        graph.replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - ts
+        us = 1e6 * wall / n
+        res[name] = {"us_per_step": round(us, 2), "GB/s": round(tot / wall / 1e9, 1),
+                     "tokens_per_s": round(wl.batch / (us * 1e-6), 1),
+                     "bytes_per_step": int(tot / n), "steps": n, "cache_copies": len(caches),
+                     "step": ("append 1 + select + decode" if appends else "select + decode"),
+                     "workload": wl.describe()}
+        log(f"{name}: {us:.1f} us/step, {tot / wall / 1e9:.0f} GB/s "
+            f"({len(caches)} copies, setup {time.time() - t0:.1f}s)")
+        del graph, caches, cache0, qs, kv, ws
+        torch.cuda.empty_cache()
+    return res
 
 if __name__ == "__main__":
     main()
