@@ -48,12 +48,17 @@ size_t ws_bytes_for(int batch, int hkv, int hq, int d, int tokens, int split) {
   return (size_t)batch * hkv * nsplit * (size_t)(hq / hkv) * dqk::partial_floats(d) * sizeof(float);
 }
 
-// Split of the 2-bit decode: the caller's, else the library's default.
-int decode_split(const dqk_cache *c, int hq, int split) {
+// Split of the 2-bit decode: the caller's, else the library's default (*even:
+// the splits take equal shares of each row's current blocks).
+int decode_split(const dqk_cache *c, int hq, int split, bool *even = nullptr) {
+  if (even) *even = false;
   if (split != 0) return split;
   const int units = c->batch * c->num_kv_heads;
-  return hq == 4 * c->num_kv_heads ? dqk::balanced_decode_split(c->capacity, units)
-                                   : dqk::default_decode_split(c->capacity, units);
+  if (hq % (4 * c->num_kv_heads) != 0) return dqk::default_decode_split(c->capacity, units);
+  const dqk::DecodeSplit d =
+      dqk::matrix_decode_split(c->capacity, units * (hq / (4 * c->num_kv_heads)));
+  if (even) *even = d.even;
+  return d.split;
 }
 
 }  // namespace
@@ -163,11 +168,12 @@ dqk_status dqk_decode_attention(const dqk_cache *cache, const float *q_prime,
   if (keep < 1 || keep > cache->head_dim) return DQK_ERR_INVALID;
   if (!isfinite(sm_scale)) return DQK_ERR_INVALID;
   if (!valid_split(split)) return DQK_ERR_INVALID;
-  const int sp = decode_split(cache, hq, split);
+  bool even = false;
+  const int sp = decode_split(cache, hq, split, &even);
   const size_t need = ws_bytes_for(cache->batch, cache->num_kv_heads, hq, cache->head_dim,
                                    cache->capacity, sp);
   if (!workspace || ws_bytes < need || !aligned16(workspace)) return DQK_ERR_WORKSPACE;
-  return from_hip(dqk::launch_decode(*cache, q_prime, sel_idx, hq, keep, sm_scale, sp, out,
+  return from_hip(dqk::launch_decode(*cache, q_prime, sel_idx, hq, keep, sm_scale, sp, even, out,
                                      static_cast<float *>(workspace),
                                      reinterpret_cast<hipStream_t>(stream)));
 }

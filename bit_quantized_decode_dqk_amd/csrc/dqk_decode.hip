@@ -579,30 +579,34 @@ hipError_t launch_decode_t(const dqk_cache &c, const float *qp, const int32_t *s
 
 template <int D>
 hipError_t launch_decode_d(const dqk_cache &c, const float *qp, const int32_t *sel, int hq,
-                           int keep, float scale2, int split, float *out, float *ws,
+                           int keep, float scale2, int split, bool even, float *out, float *ws,
                            hipStream_t s) {
   switch (hq / c.num_kv_heads) {
     case 1: return launch_decode_t<D, 1>(c, qp, sel, hq, keep, scale2, split, out, ws, s);
     case 2: return launch_decode_t<D, 2>(c, qp, sel, hq, keep, scale2, split, out, ws, s);
-    case 4: {
-      if (!decode4_supported(c))
-        return launch_decode_t<D, 4>(c, qp, sel, hq, keep, scale2, split, out, ws, s);
-      const hipError_t e = launch_decode4(c, qp, sel, hq, keep, scale2, split, ws, s);
+    case 4:
+    case 8: {
+      if (!decode4_supported(c, hq))
+        return hq == 4 * c.num_kv_heads
+                   ? launch_decode_t<D, 4>(c, qp, sel, hq, keep, scale2, split, out, ws, s)
+                   : launch_decode_t<D, 8>(c, qp, sel, hq, keep, scale2, split, out, ws, s);
+      const hipError_t e = launch_decode4(c, qp, sel, hq, keep, scale2, split, even, ws, s);
       if (e != hipSuccess) return e;
       return launch_combine(ws, c.batch, hq, c.num_kv_heads, D, num_splits(c.capacity, split), out, s);
     }
-    default: return launch_decode_t<D, 8>(c, qp, sel, hq, keep, scale2, split, out, ws, s);
+    default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
 hipError_t launch_decode(const dqk_cache &c, const float *q_prime, const int32_t *sel_idx, int hq,
-                         int keep, float sm_scale, int split, float *out, float *ws,
+                         int keep, float sm_scale, int split, bool even, float *out, float *ws,
                          hipStream_t s) {
   const float scale2 = sm_scale * 1.4426950408889634f;  // logits in log2 units
-  if (c.head_dim == 64) return launch_decode_d<64>(c, q_prime, sel_idx, hq, keep, scale2, split, out, ws, s);
-  return launch_decode_d<128>(c, q_prime, sel_idx, hq, keep, scale2, split, out, ws, s);
+  if (c.head_dim == 64)
+    return launch_decode_d<64>(c, q_prime, sel_idx, hq, keep, scale2, split, even, out, ws, s);
+  return launch_decode_d<128>(c, q_prime, sel_idx, hq, keep, scale2, split, even, out, ws, s);
 }
 
 }  // namespace dqk

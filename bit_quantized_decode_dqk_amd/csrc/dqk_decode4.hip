@@ -1,5 +1,6 @@
 // Decode attention over the 2-bit cache for GQA groups of four query heads
-// (hq / hkv == 4), both contractions on the matrix cores.
+// (hq / hkv == 4, or a multiple of four served four heads per workgroup), both
+// contractions on the matrix cores.
 //
 // Dual-QK (arXiv abstract; tech.dede.sh summary, "Throughput on SGLang"): keys
 // and values are stored in 2 bits and the key channels a query head does not
@@ -57,7 +58,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 half2 __attribute__((ext_vector_type(2)));
 typedef float float2v __attribute__((ext_vector_type(2)));
 
-constexpr int kG4 = 4;              // query heads per KV head
+constexpr int kG4 = 4;              // query heads per workgroup (a slice of the KV head's group)
 constexpr int kThreads4 = 256;
 constexpr int kWaves4 = kThreads4 / 64;
 constexpr int kTile4 = 64;          // tokens per wavefront tile: two key groups
@@ -260,13 +261,24 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
   __shared__ Smem4<D> sm;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: block and tile offsets stay scalar
-  // Split-major order: workgroups of one split index run together.
+  // Work item (unit, split s) in split-major order: workgroups of one split index
+  // run together.  A KV head with more than four query heads is served in slices
+  // of four, one workgroup each; the slices of one work item get workgroup ids
+  // eight apart, which go to the same XCD (workgroups are dealt round-robin over
+  // the eight XCDs), so a later slice finds the item's bytes in that XCD's L2.
   const int units = c.batch * c.num_kv_heads;
-  const int unit = blockIdx.x % units, s = blockIdx.x / units;
+  const int nsl = hq / (c.num_kv_heads * G);
+  int item = blockIdx.x, slice = 0;
+  if (nsl > 1) {
+    slice = (blockIdx.x >> 3) % nsl;
+    item = (blockIdx.x / (8 * nsl)) * 8 + (blockIdx.x & 7);
+    if (item >= units * nsplit) return;   // the grid is padded to whole groups of eight items
+  }
+  const int unit = item % units, s = item / units;
   const int b = unit / c.num_kv_heads, g = unit % c.num_kv_heads;
-  // The group's q' rows (all channels) and kept-channel lists are loaded before
+  // The slice's q' rows (all channels) and kept-channel lists are loaded before
   // anything waits, in parallel with the length: one round trip for the setup.
-  const size_t row0 = (size_t)b * hq + (size_t)g * G;
+  const size_t row0 = (size_t)b * hq + (size_t)g * G * nsl + (size_t)G * slice;
   constexpr int SJ = (G * D) / kThreads4;   // elements per lane
   float qv[SJ];
   int sv[SJ];
@@ -285,7 +297,7 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
   const int t_begin = blo * kBlock4;
   const int t_end = min(bhi * kBlock4, len);
   const int nb = bhi - blo;
-  float *wsp = ws + ((size_t)unit * nsplit + s) * G * (D + kPartialHead);
+  float *wsp = ws + (((size_t)unit * nsplit + s) * nsl + slice) * G * (D + kPartialHead);
   if (t_begin >= t_end) {
     for (int e = tid; e < G * (D + kPartialHead); e += kThreads4)
       wsp[e] = (e % (D + kPartialHead) == 0) ? -INFINITY : 0.0f;
@@ -903,15 +915,20 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
 
 }  // namespace
 
-bool decode4_supported(const dqk_cache &c) { return c.capacity % 64 == 0; }
+bool decode4_supported(const dqk_cache &c, int hq) {
+  return c.capacity % 64 == 0 && hq % (c.num_kv_heads * kG4) == 0;
+}
 
 hipError_t launch_decode4(const dqk_cache &c, const float *q_prime, const int32_t *sel_idx, int hq,
-                          int keep, float scale2, int split, float *ws, hipStream_t s) {
+                          int keep, float scale2, int split, bool even, float *ws, hipStream_t s) {
   const int nsplit = num_splits(c.capacity, split);
-  // a split of whole blocks covers exactly its split tokens of every row
-  const int bps = split % kBlock4 == 0 ? split / kBlock4 : 0;
+  // a caller's split of whole blocks covers exactly its split tokens of every row;
+  // otherwise (and always for the library's own split count) each split takes an
+  // equal share of its row's current blocks
+  const int bps = !even && split % kBlock4 == 0 ? split / kBlock4 : 0;
   const int items = c.batch * c.num_kv_heads * nsplit;
-  const dim3 grid((unsigned)items), block(kThreads4);
+  const int nsl = hq / (c.num_kv_heads * kG4);
+  const dim3 grid((unsigned)(nsl > 1 ? (items + 7) / 8 * 8 * nsl : items)), block(kThreads4);
   if (c.head_dim == 64)
     hipLaunchKernelGGL((decode4_kernel<64>), grid, block, 0, s, c, q_prime, sel_idx, hq, keep, scale2, nsplit,
                        bps, ws);

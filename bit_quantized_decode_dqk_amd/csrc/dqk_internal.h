@@ -18,14 +18,31 @@ constexpr int kDefaultSplit = 1024; // bf16 decode split length when the caller 
 // Groups of four query heads share the sequence by length (each workgroup takes
 // an equal share of the current tokens): the default only fixes the number of
 // splits, about two workgroups per compute unit, with at least 256 tokens of
-// capacity per split.
-inline int balanced_decode_split(int capacity, int units) {
-  int nsplit = 512 / units;
+// capacity per split.  `workgroups` is the number of workgroups per split index
+// (units times the four-head slices of a group).
+inline int balanced_decode_split(int capacity, int workgroups) {
+  int nsplit = 512 / workgroups;
   if (nsplit < 1) nsplit = 1;
   const int most = (capacity + 255) / 256;
   if (nsplit > most) nsplit = most;
   const int split = (capacity + nsplit - 1) / nsplit;
   return (split + 31) / 32 * 32;
+}
+
+// Default split of the matrix-core decode.  When the capacity alone gives more
+// than 16 blocks of 256 tokens per resident workgroup slot (512), fixed splits of
+// 16 whole blocks: work items then outnumber the slots several times and the
+// dispatcher evens out rows of different lengths.  Otherwise the balanced split
+// count above, each split taking an equal share of its row's current blocks
+// (even = true).
+struct DecodeSplit {
+  int split;
+  bool even;
+};
+inline DecodeSplit matrix_decode_split(int capacity, int workgroups) {
+  const long long blocks = (long long)workgroups * ((capacity + 255) / 256);
+  if (blocks > 16LL * 512) return {16 * 256, false};
+  return {balanced_decode_split(capacity, workgroups), true};
 }
 
 inline int default_decode_split(int capacity, int units) {
@@ -79,12 +96,15 @@ hipError_t launch_append_select(const dqk_cache &c, const void *k_new, const voi
                                 bool bf16, const float *bmat, const int32_t *n_new, int max_new,
                                 const void *q, const float *amat, int hq, int keep,
                                 float *q_prime, int32_t *sel_idx, hipStream_t s);
+// even: the split length is the library's choice (each split then takes an equal
+// share of its row's current blocks), not the caller's
 hipError_t launch_decode(const dqk_cache &c, const float *q_prime, const int32_t *sel_idx, int hq,
-                         int keep, float sm_scale, int split, float *out, float *ws,
+                         int keep, float sm_scale, int split, bool even, float *out, float *ws,
                          hipStream_t s);
-bool decode4_supported(const dqk_cache &c);
+// the matrix-core decode: groups of a multiple of four query heads, capacity a multiple of 64
+bool decode4_supported(const dqk_cache &c, int hq);
 hipError_t launch_decode4(const dqk_cache &c, const float *q_prime, const int32_t *sel_idx, int hq,
-                          int keep, float scale2, int nsplit, float *ws, hipStream_t s);
+                          int keep, float scale2, int split, bool even, float *ws, hipStream_t s);
 hipError_t launch_dequant(const dqk_cache &c, float *k_out, float *v_out, hipStream_t s);
 hipError_t launch_bf16_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                               const int32_t *lengths, int batch, int hq, int hkv, int d, int ld_t,

@@ -81,18 +81,27 @@ def test_cache_validation_without_gpu():
 
 def test_default_split_for_groups_of_four():
     """Default split of the four-head decode, read back through the workspace
-    size (one partial of 4 heads x (d + 4) floats per split and (row, KV head)):
+    size (one partial of G heads x (d + 4) floats per split and (row, KV head)):
     about 512 workgroups (two per compute unit on 256), at least 256 tokens of
-    capacity each."""
+    capacity each, unless the capacity alone gives more than 16 blocks per slot.
+    Groups of eight run as two four-head workgroups per split."""
     L = M.lib()
     out = C.c_size_t(0)
 
-    def splits(batch, hkv, cap):
+    def splits(batch, hkv, cap, group=4):
         c = fake_cache(batch=batch, num_kv_heads=hkv, capacity=cap)
-        assert L.dqk_decode_workspace_bytes(C.byref(c), 4 * hkv, 0, C.byref(out)) == OK
-        per = batch * hkv * 4 * 132 * 4
+        assert L.dqk_decode_workspace_bytes(C.byref(c), group * hkv, 0, C.byref(out)) == OK
+        per = batch * hkv * group * 132 * 4
         assert out.value % per == 0
         return out.value // per
+
+    # more than 16 blocks per slot of 512 from the capacity alone: whole-block
+    # splits of 16 blocks (4096 tokens)
+    assert splits(16, 8, 65536, 8) == 16       # 128 units x 2 slices x 256 blocks
+    assert splits(8, 8, 131072) == 32          # 64 units x 512 blocks
+    assert splits(8, 8, 32768) == 8            # 64 x 128 blocks = 8192: balanced, 8 per unit
+    assert splits(1, 8, 131072, 8) == 32
+    assert splits(1, 1, 4096, 8) == 16
 
     assert splits(1, 8, 131072) == 64
     assert splits(1, 8, 131328) == 64          # 513 blocks: one split of nine

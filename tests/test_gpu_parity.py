@@ -263,11 +263,14 @@ def test_decode_group4_nine_block_chunks(orc):
 
 
 @pytest.mark.parametrize("hq,hkv,lens", [(4, 1, [3000, 1200, 64]), (12, 3, [2500]),
-                                          (20, 5, [1800, 4000])])
+                                          (20, 5, [1800, 4000]), (8, 1, [3000, 1200, 64]),
+                                          (24, 3, [2500]), (40, 5, [1800, 4000])])
 def test_decode_group4_unit_counts(orc, hq, hkv, lens):
-    """Groups of four with (row, KV head) counts that are not multiples of
-    eight: the splits of one row and KV head run on different parts of the chip,
-    and the last to finish merges the others' partials."""
+    """Groups of four (and of eight, two four-head workgroups per split) with
+    (row, KV head) counts that are not multiples of eight: the splits of one row
+    and KV head run on different parts of the chip, the grid of a group of eight
+    is padded to whole groups of eight work items, and the combine joins the
+    partials."""
     wl = W.custom(f"g4-u{hkv}", 30 + hkv, len(lens), hq, hkv, 128, lens, 4032, "bf16",
                   log_uniform_key_scales=True)
     decode_case(orc, wl, splits=(0, 64, 256, 1024))
@@ -351,6 +354,64 @@ def test_decode_ctx128k_sampled(orc):
             err = rel_err(out[:, hs], ocs[g].decode(qpo, idxo, sm))
             say(f"  length {ctx + extra}, KV head {g}: max rel err {err:.3e}")
             assert err <= REL_TOL, (extra, g, err)
+
+
+def test_decode_ragged64k_sampled(orc):
+    """The ragged group-of-eight workload at full size (batch 16, 64/8 heads,
+    head_dim 128, rows of 20K..62K tokens in a 64K capacity, 40% sparsity,
+    Student-t queries) in its launch configuration: the default split, here
+    whole-block splits of 16 blocks with two four-head workgroups per split (and
+    an equal-share split for comparison).  Three (row, KV head) units are checked
+    against the oracle: the longest row, the shortest and a middle one.  They hold
+    the workload's own keys and values; the other units hold normal draws of the
+    same channel scales (the units are independent)."""
+    wl = W.workload("ragged64k")
+    lens = np.array(wl.ctx)
+    sm = W.default_sm_scale(wl.d)
+    a, b = W.transforms(wl)
+    kscale = W.key_scales(wl)
+    order = np.argsort(lens, kind="stable")
+    units = [(int(order[-1]), 0), (int(order[0]), 7), (int(order[len(order) // 2]), 3)]
+    say("ragged64k sampled: lengths", int(lens.min()), "..", int(lens.max()), "units", units)
+    kv = {u: W.unit_kv(wl, u[0], u[1], 0, int(lens[u[0]]), kscale) for u in units}
+    cache = M.Cache(wl.batch, wl.hkv, wl.d, wl.cap)
+    bm, ks_d = dev_f32(b), dev_f32(kscale)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(11)
+    chunk = 8192
+    for pos in range(0, int(lens.max()), chunk):
+        nn = np.clip(lens - pos, 0, chunk).astype(np.int32)
+        k = torch.randn((wl.batch, wl.hkv, chunk, wl.d), generator=gen, device="cuda")
+        k = (k * ks_d[None, :, None, :]).to(torch.bfloat16)
+        v = torch.randn((wl.batch, wl.hkv, chunk, wl.d), generator=gen, device="cuda").to(torch.bfloat16)
+        for (bb, g), (kk, vv) in kv.items():
+            m = int(nn[bb])
+            if m > 0:   # exact bf16 values: the conversion is exact
+                k[bb, g, :m] = torch.from_numpy(kk[pos:pos + m]).cuda().to(torch.bfloat16)
+                v[bb, g, :m] = torch.from_numpy(vv[pos:pos + m]).cuda().to(torch.bfloat16)
+        M.transform_quantize_append(cache, k, v, bm, dev_i32(nn))
+    keep = orc.keep_count(wl.d, 40)
+    q = W.queries(wl)
+    qp, idx = gpu_queries(wl, q, a, keep)
+    idx_np = idx.cpu().numpy()
+    refs = {}
+    for (bb, g), (kk, vv) in kv.items():
+        say(f"  oracle: row {bb} ({int(lens[bb])} tokens), KV head {g}")
+        oc = orc.Cache(1, 1, wl.d, wl.cap)
+        oc.append(kk[None, None], vv[None, None], b[g:g + 1], [int(lens[bb])])
+        hs = slice(8 * g, 8 * g + 8)
+        qpo, idxo = orc.queries(q[bb:bb + 1, hs], a[g:g + 1], 1, keep)
+        assert np.array_equal(idx_np[bb:bb + 1, hs], idxo), (bb, g)
+        refs[(bb, g)] = oc.decode(qpo, idxo, sm)
+    outs = {}
+    for sp in (0, 4096, 8224):
+        outs[sp] = out = M.decode_attention(cache, qp, idx, sm, split_tokens=sp).cpu().numpy()
+        for (bb, g), ref in refs.items():
+            err = rel_err(out[bb:bb + 1, 8 * g:8 * g + 8], ref)
+            say(f"  split {sp}, row {bb}, KV head {g}: max rel err {err:.3e}")
+            assert err <= REL_TOL, (sp, bb, g, err)
+    # the default is whole-block splits of 4096 tokens here: the same launch
+    assert np.array_equal(outs[0].view(np.uint32), outs[4096].view(np.uint32))
 
 
 def test_step_graph_replay_matches_eager(orc):
