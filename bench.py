@@ -378,6 +378,7 @@ def main():
         extras = run_extras(M, torch, wl, caches, a_d, step_q, qp, idx, out, ws, k_d, v_d, sm,
                             args, roof_us)
         extras["other_workloads"] = run_configs(M, torch)
+        extras["stream_peak"] = stream_peak(M, torch)
 
     result = {
         "metric": "decode attention effective HBM GB/s + tokens/s at 128K ctx, INT2, 40% sparsity",
@@ -473,6 +474,34 @@ def run_extras(M, torch, wl, caches, a_d, step_q, qp, idx, out, ws, k_d, v_d, sm
     del k2, v2
     return res
 
+
+
+def stream_peak(M, torch, mib: int = 4096, reps: int = 10):
+    """Practical HBM ceilings on a 4 GiB buffer (far past the 256 MB Infinity
+    Cache): the library's plain streaming-read kernel, and a device copy (read +
+    write, torch), both in GB/s of bytes moved.  Context for the roofline
+    fraction."""
+    n = (mib << 20) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    sink = torch.empty(M.STREAM_READ_SINK_WORDS, dtype=torch.int32, device="cuda")
+    res = {}
+    for name, fn, moved in (("read", lambda: M.stream_read(x, sink), 4 * n),
+                            ("copy", lambda: y.copy_(x), 8 * n)):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[f"{name}_GB/s"] = round(moved * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    del x, y
+    torch.cuda.empty_cache()
+    log(f"stream peak: {res}")
+    return res
 
 
 def run_configs(M, torch, steps: int = 32):

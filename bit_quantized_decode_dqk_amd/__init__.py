@@ -35,7 +35,7 @@ EXPORTS = ("dqk_status_str", "dqk_cache_plane_bytes", "dqk_transform_quantize_ap
            "dqk_select_channels", "dqk_append_select", "dqk_decode_workspace_bytes",
            "dqk_decode_attention",
            "dqk_dequant_reference", "dqk_bf16_decode_workspace_bytes",
-           "dqk_bf16_decode_attention", "dqk_debug_f16_from_f32")
+           "dqk_bf16_decode_attention", "dqk_debug_f16_from_f32", "dqk_stream_read")
 
 
 def lib():
@@ -60,6 +60,7 @@ def lib():
             "dqk_bf16_decode_workspace_bytes": [I, I, I, I, I, I, P],
             "dqk_bf16_decode_attention": [P, P, P, P, I, I, I, I, I, C.c_float, I, P, P, S, P],
             "dqk_debug_f16_from_f32": [P, P, S, P],
+            "dqk_stream_read": [P, S, P, P],
         }.items():
             fn = getattr(L, name)
             fn.restype = C.c_int
@@ -273,3 +274,18 @@ def debug_f16_from_f32(x, stream=None):
     _check(lib().dqk_debug_f16_from_f32(_ptr(x), _ptr(out), x.numel(), _stream(stream)),
            "dqk_debug_f16_from_f32")
     return out
+
+
+STREAM_READ_SINK_WORDS = 8192
+
+
+def stream_read(buf, sink=None, stream=None):
+    """Read every byte of the device tensor `buf` once (a plain streaming kernel;
+    a measurement aid).  Returns the sink [8192] int32 tensor, whose XOR is the XOR
+    of the buffer's 32-bit words."""
+    torch = _torch()
+    if sink is None:
+        sink = torch.empty(STREAM_READ_SINK_WORDS, dtype=torch.int32, device=buf.device)
+    _check(lib().dqk_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                 _stream(stream)), "dqk_stream_read")
+    return sink

@@ -31,6 +31,7 @@ SOURCES = {
     "dqk_decode4.hip": ["-fno-honor-nans"],
     "dqk_bf16.hip": [],
     "dqk_combine.hip": [],
+    "dqk_probe.hip": [],
 }
 
 COMMON = ["-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",

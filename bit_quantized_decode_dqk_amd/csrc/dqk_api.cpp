@@ -218,4 +218,10 @@ dqk_status dqk_debug_f16_from_f32(const float *x, uint16_t *out, size_t n, dqk_s
   return from_hip(dqk::launch_f16_convert(x, out, n, reinterpret_cast<hipStream_t>(stream)));
 }
 
+dqk_status dqk_stream_read(const void *buf, size_t bytes, uint32_t *sink, dqk_stream_t stream) {
+  if (!sink || !aligned16(sink) || bytes % 16 != 0) return DQK_ERR_INVALID;
+  if (bytes > 0 && (!buf || !aligned16(buf))) return DQK_ERR_INVALID;
+  return from_hip(dqk::launch_stream_read(buf, bytes, sink, reinterpret_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

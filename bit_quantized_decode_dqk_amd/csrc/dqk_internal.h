@@ -112,6 +112,8 @@ hipError_t launch_bf16_decode(const uint16_t *q, const uint16_t *k, const uint16
 hipError_t launch_combine(const float *ws, int batch, int hq, int hkv, int d, int nsplit,
                           float *out, hipStream_t s);
 hipError_t launch_f16_convert(const float *x, uint16_t *out, size_t n, hipStream_t s);
+constexpr int kStreamReadSinkWords = DQK_STREAM_READ_SINK_WORDS;   // 2048 workgroups x 4 wavefronts
+hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t s);
 
 // Workspace: per work item (unit, split) and query head of its group:
 // m, l, two pad floats (keeps o 16-byte aligned), o[d].

@@ -183,6 +183,19 @@ dqk_status dqk_bf16_decode_attention(const uint16_t *q, const uint16_t *k, const
 dqk_status dqk_debug_f16_from_f32(const float *x, uint16_t *out, size_t n,
                                   dqk_stream_t stream);
 
+/* Measurement aid, not part of the method: reads `bytes` of device memory at buf
+ * once with 16-byte loads (a plain streaming kernel, 2048 workgroups of 256
+ * threads) and leaves in sink a fold of what it read: the XOR of the
+ * DQK_STREAM_READ_SINK_WORDS sink words equals the XOR of every 32-bit word of
+ * the buffer.  Its run time over a buffer far larger than the 256 MB Infinity
+ * Cache gives the read rate a plain kernel reaches, against which the decode's
+ * byte rate is read.  buf: 16-byte aligned, bytes a multiple of 16 (0 is a valid
+ * no-op read that still writes zeros); sink: device u32 [DQK_STREAM_READ_SINK_WORDS],
+ * every word overwritten.  Errors: DQK_ERR_INVALID for null or misaligned
+ * pointers or sizes. */
+#define DQK_STREAM_READ_SINK_WORDS 8192
+dqk_status dqk_stream_read(const void *buf, size_t bytes, uint32_t *sink, dqk_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -128,6 +128,18 @@ def test_decode_validation_without_gpu():
     assert L.dqk_decode_attention(c, q, idx, 8, 77, 0.1, 0, out, ws + 4, big, None) == WORKSPACE
 
 
+def test_stream_read_validation_without_gpu():
+    """The read probe rejects null or misaligned pointers and sizes that are not
+    whole 16-byte elements before launching anything."""
+    L = M.lib()
+    buf, sink = 0x20000, 0x30000
+    assert L.dqk_stream_read(buf, 1 << 20, None, None) == INVALID
+    assert L.dqk_stream_read(buf, 1 << 20, sink + 4, None) == INVALID
+    assert L.dqk_stream_read(buf, (1 << 20) + 8, sink, None) == INVALID
+    assert L.dqk_stream_read(None, 1 << 20, sink, None) == INVALID
+    assert L.dqk_stream_read(buf + 8, 1 << 20, sink, None) == INVALID
+
+
 def test_append_select_dequant_validation_without_gpu():
     L = M.lib()
     c = C.byref(fake_cache())

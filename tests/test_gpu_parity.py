@@ -496,6 +496,22 @@ def test_decode_deterministic(orc):
 
 # ----------------------------------------------------------------------------- bf16 comparator
 
+
+@pytest.mark.parametrize("nbytes", [0, 16, 4096 + 48, (64 << 20) + 16 * 777])
+def test_stream_read_folds_every_word(nbytes):
+    """The read probe reads each 16-byte element exactly once: the XOR of its
+    sink equals the XOR of the buffer's 32-bit words (sizes below one load per
+    thread, two iterations of the unrolled loop and a ragged tail, and empty)."""
+    rng = np.random.default_rng(nbytes)
+    words = rng.integers(0, 1 << 32, size=nbytes // 4, dtype=np.uint64).astype(np.uint32)
+    buf = torch.from_numpy(words.view(np.int32)).cuda() if nbytes else torch.empty(0, dtype=torch.int32, device="cuda")
+    sink = torch.full((M.STREAM_READ_SINK_WORDS,), -1, dtype=torch.int32, device="cuda")
+    M.stream_read(buf, sink)
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    want = np.bitwise_xor.reduce(words) if nbytes else np.uint32(0)
+    assert got == want, (nbytes, hex(int(got)), hex(int(want)))
+
+
 @pytest.mark.parametrize("lens,sm_mult", [([4096], 1.0), ([4096], 0.02), ([1000, 1, 0, 2049], 0.05)])
 def test_bf16_decode_matches_plain_attention(orc, lens, sm_mult):
     wl = W.custom("bf16cmp", 26, len(lens), 32, 8, 128, lens, 4096 + 64, "bf16",
