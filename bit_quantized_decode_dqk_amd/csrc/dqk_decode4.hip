@@ -124,8 +124,7 @@ struct __attribute__((aligned(16))) Smem4 {
     uint8_t b[kG4][D];        // kept[h][c]: head h keeps channel c
     uint32_t w[kG4 * D / 4];
   } kept;
-  int16_t ulist[D];
-  int wcount[2];
+  unsigned long long umask[2];   // the union U of kept key channels >= 1: bit c of word c / 64
 };
 
 // Registers of one block of keys in flight.
@@ -315,72 +314,6 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
   const int t_body = (len / kGroup) * kGroup;
   const int code_end = min(t_body, t_end);
 
-  // ---------------------------------------------------------------- setup (whole workgroup)
-  for (int e = tid; e < G * D / 4; e += kThreads4) sm.kept.w[e] = 0u;
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < SJ; ++k) {
-    const int e = tid + kThreads4 * k;
-    if (e < G * keep && sv[k] >= 0 && sv[k] < D) sm.kept.b[e / keep][sv[k]] = 1;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < SJ; ++k) {
-    // head h and half of element e are the same for the whole wavefront
-    const int e = tid + kThreads4 * k, h = e / D, ch = e % D;
-    const float cv = sm.kept.b[h][ch] ? qv[k] * scale2 : 0.0f;
-    sm.coefc[h][ch] = cv;
-    const float mx = wave_max(ch >= 1 ? fabsf(cv) : 0.0f);   // largest |coefficient| over channels >= 1
-    if (lane == 0) sm.redm[h][ch / 64] = mx;
-  }
-  {
-    const bool f = tid >= 1 && tid < D &&
-                   (sm.kept.b[0][tid % D] | sm.kept.b[1][tid % D] | sm.kept.b[2][tid % D] | sm.kept.b[3][tid % D]);
-    const unsigned long long m = __ballot(f);
-    if (lane == 0 && wave < 2) sm.wcount[wave] = __popcll(m);
-    __syncthreads();
-    if (f) sm.ulist[__popcll(m & ((1ull << lane) - 1ull)) + (wave == 1 ? sm.wcount[0] : 0)] = (int16_t)tid;
-  }
-  __syncthreads();
-  const int nu = sm.wcount[0] + sm.wcount[1];
-  const int nkc = (nu + 15) / 16;
-  // Tokens of the unfinished last key group (only in the workgroup that reaches
-  // it): exact logits from the fp32 tail keys, one per (head, token).
-  // The tail rows are staged in LDS first (the key block buffers are free until
-  // the first block): one round trip instead of one per channel.
-  // Every channel is summed in ascending order: a channel the head drops has
-  // coefficient 0 and adds exactly nothing.  Rows are padded to D + 4 floats so
-  // that the rows of a wavefront's lanes fall in different LDS banks.
-  if (t_body < t_end) {
-    constexpr int TS = D + 4;
-    static_assert(sizeof(sm.kb[0]) >= sizeof(float) * kGroup * TS, "tail rows fit a key block buffer");
-    float *trow = reinterpret_cast<float *>(&sm.kb[0]);
-#pragma unroll
-    for (int k = 0; k < kGroup * D / (4 * kThreads4); ++k) {
-      const int e = 4 * (tid + kThreads4 * k);
-      *reinterpret_cast<f32x4 *>(trow + (e / D) * TS + e % D) = *reinterpret_cast<const f32x4 *>(tail + e);
-    }
-    const int h = (tid / kGroup) % G, r = tid % kGroup, t = t_body + r;
-    const float c0 = f16_value(c0row[min(t, t_end - 1)]);
-    __syncthreads();
-    if (tid < G * kGroup) {
-      float zz = -INFINITY;
-      if (t < t_end) {
-        zz = sm.coefc[h][0] * c0;   // channel 0: its fp16 value, as in the blocks
-#pragma unroll
-        for (int c4 = 0; c4 < D; c4 += 4) {
-          const f32x4 cf = *reinterpret_cast<const f32x4 *>(&sm.coefc[h][c4]);
-          const f32x4 x = *reinterpret_cast<const f32x4 *>(&trow[r * TS + c4]);
-          if (c4 > 0) zz = fmaf(cf.x, x.x, zz);
-          zz = fmaf(cf.y, x.y, zz);
-          zz = fmaf(cf.z, x.z, zz);
-          zz = fmaf(cf.w, x.w, zz);
-        }
-      }
-      sm.tailz[h][r] = zz;
-    }
-  }
-  __syncthreads();
   // Loads go through buffer resources of the unit's planes whose base is moved
   // to the block or tile (scalar arithmetic; the per-lane offsets stay fixed):
   // an offset past the resource returns zero, so absent parts point past the
@@ -394,17 +327,47 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
                                              live ? (int)(bytes - off) : 0, kRsrcWord3);
   };
 
+  // Rows of the unfinished last key group, only in the workgroup that reaches it
+  // (elsewhere the resource is empty and the loads move no bytes): issued before
+  // the key blocks, so that staging them waits for nothing else.
+  const bool has_tail = t_body < t_end;
+  constexpr int TJ = kGroup * D / (4 * kThreads4);   // float4 per lane
+  f32x4 tv[TJ];
+  {
+    const auto rt = rsrc(tail, (uint32_t)(kGroup * D * 4), 0u, has_tail);
+#pragma unroll
+    for (int k = 0; k < TJ; ++k)
+      tv[k] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rt, 16u * (tid + kThreads4 * k), 0, 0));
+  }
+
   // ---------------------------------------------------------------- key loads (every lane)
+  // Union slot i holds key channel i + 1 (the last slot is empty), so the layout
+  // of a block does not depend on the selection: the first block is issued for
+  // every channel as soon as the length is known, and its latency overlaps the
+  // setup below.  Once the union U of the group's kept channels is known, the
+  // channels outside it point past the plane (zero codes, no bytes) for the later
+  // blocks; their coefficients are zero, so the extra bytes of the first block
+  // change no result.
   // Every lane has one job of each kind, so that no write to LDS depends on the
   // lane; at head_dim 64 the upper lanes repeat the key-code jobs of the lower
   // ones (the same bytes to the same place).
   // key codes: slot octet lo, 16-token quarter lq of the block; 8 slots x 4 bytes
+  // Offsets in 32-bit arithmetic (a plane of a unit is below 4 GiB).  The products
+  // are kept apart from the additions: fused, they become a 64-bit multiply-add
+  // whose unused high addend may be any register, also one a setup load is still
+  // writing, and the key loads would then wait for that load.
+  auto mul_apart = [](uint32_t a, uint32_t b) {
+    uint32_t p = a * b;
+    asm volatile("" : "+v"(p));
+    return p;
+  };
   const int lo = (tid >> 4) % L::OCT, lq = tid & 15;
+  const uint32_t kc_row = (uint32_t)kc_stride, ks_row = 2u * (uint32_t)ks_stride;
   uint32_t kvo[8];
 #pragma unroll
   for (int cc = 0; cc < 8; ++cc) {
-    const int i = 8 * lo + cc;
-    kvo[cc] = i < nu ? (uint32_t)(sm.ulist[i] * kc_stride) + 4u * lq : kFar;
+    const int ch = 8 * lo + cc + 1;
+    kvo[cc] = ch < D ? mul_apart((uint32_t)ch, kc_row) + 4u * (uint32_t)lq : kFar;
   }
   // logit A operands, built here from the key scales: job j (one per lane; the
   // upper lanes repeat the lower ones at head_dim 64) is key-group pair gp = tile
@@ -414,8 +377,8 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
   const int aoct = asp >> 2, am = asp & 3;
   const int as0 = 8 * aoct + (am & 1) + 4 * (am >> 1), as1 = as0 + 2;
   uint32_t ksv[2];
-  ksv[0] = as0 < nu ? (uint32_t)(sm.ulist[as0] * ks_stride * 2) + 4u * agp : kFar;
-  ksv[1] = as1 < nu ? (uint32_t)(sm.ulist[as1] * ks_stride * 2) + 4u * agp : kFar;
+  ksv[0] = as0 + 1 < D ? mul_apart((uint32_t)(as0 + 1), ks_row) + 4u * (uint32_t)agp : kFar;
+  ksv[1] = as1 + 1 < D ? mul_apart((uint32_t)(as1 + 1), ks_row) + 4u * (uint32_t)agp : kFar;
   // channel 0: dword tid (tokens 2 tid, 2 tid + 1) for the lower 128 lanes
   const uint32_t c0o = tid < kBlock4 / 2 ? 4u * tid : kFar;
 
@@ -438,28 +401,101 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // The first chunk's first two blocks are issued now, before the coefficients are
-  // worked out: their latency overlaps the rest of the
-  // setup.
   const int nbc0 = nb == kChunk4 + 1 ? kChunk4 + 1 : min(kChunk4, nb);
   KStage4<D> S0, S1;
   kissue(S0, t_begin, 0 < nbc0);
-  kissue(S1, t_begin + kBlock4, 1 < nbc0);
+
+  // ---------------------------------------------------------------- setup (whole workgroup)
+  // Barriers here order LDS only (block_barrier): a full __syncthreads would also
+  // wait for the blocks just issued.
+  for (int e = tid; e < G * D / 4; e += kThreads4) sm.kept.w[e] = 0u;
+  block_barrier();
+#pragma unroll
+  for (int k = 0; k < SJ; ++k) {
+    const int e = tid + kThreads4 * k;
+    if (e < G * keep && sv[k] >= 0 && sv[k] < D) sm.kept.b[e / keep][sv[k]] = 1;
+  }
+  block_barrier();
+#pragma unroll
+  for (int k = 0; k < SJ; ++k) {
+    // head h and half of element e are the same for the whole wavefront
+    const int e = tid + kThreads4 * k, h = e / D, ch = e % D;
+    const float cv = sm.kept.b[h][ch] ? qv[k] * scale2 : 0.0f;
+    sm.coefc[h][ch] = cv;
+    const float mx = wave_max(ch >= 1 ? fabsf(cv) : 0.0f);   // largest |coefficient| over channels >= 1
+    if (lane == 0) sm.redm[h][ch / 64] = mx;
+  }
+  {
+    // the union U: bit c of umask for key channel c >= 1 kept by some head of the group
+    const bool f = tid >= 1 && tid < D &&
+                   (sm.kept.b[0][tid % D] | sm.kept.b[1][tid % D] | sm.kept.b[2][tid % D] | sm.kept.b[3][tid % D]);
+    const unsigned long long m = __ballot(f);
+    if (lane == 0 && wave < 2) sm.umask[wave] = m;
+  }
+  // Tail rows to LDS (the key block buffers are free until the first block),
+  // padded to D + 4 floats so that the rows of a wavefront's lanes fall in
+  // different banks.
+  constexpr int TS = D + 4;
+  static_assert(sizeof(sm.kb[0]) >= sizeof(float) * kGroup * TS, "tail rows fit a key block buffer");
+  float *trow = reinterpret_cast<float *>(&sm.kb[0]);
+  if (has_tail) {
+#pragma unroll
+    for (int k = 0; k < TJ; ++k) {
+      const int e = 4 * (tid + kThreads4 * k);
+      *reinterpret_cast<f32x4 *>(trow + (e / D) * TS + e % D) = tv[k];
+    }
+  }
+  block_barrier();
+  // Tokens of the unfinished last key group: exact logits from the fp32 tail
+  // keys, one per (head, token).  Every channel is summed in ascending order: a
+  // channel the head drops has coefficient 0 and adds exactly nothing.
+  if (has_tail && tid < G * kGroup) {
+    const int h = tid / kGroup, r = tid % kGroup, t = t_body + r;
+    float zz = -INFINITY;
+    if (t < t_end) {
+      zz = sm.coefc[h][0] * f16_value(c0row[t]);   // channel 0: its fp16 value, as in the blocks
+#pragma unroll
+      for (int c4 = 0; c4 < D; c4 += 4) {
+        const f32x4 cf = *reinterpret_cast<const f32x4 *>(&sm.coefc[h][c4]);
+        const f32x4 x = *reinterpret_cast<const f32x4 *>(&trow[r * TS + c4]);
+        if (c4 > 0) zz = fmaf(cf.x, x.x, zz);
+        zz = fmaf(cf.y, x.y, zz);
+        zz = fmaf(cf.z, x.z, zz);
+        zz = fmaf(cf.w, x.w, zz);
+      }
+    }
+    sm.tailz[h][r] = zz;
+  }
+  // coefficients in slot order, scaled by 2^-E_h (E_h: exponent of the head's
+  // largest |coefficient| over channels >= 1); slot i is channel i + 1
   for (int e = tid; e < G * D; e += kThreads4) {
     const int h = e / D, i = e % D;
     const float mx = D > 64 ? fmaxf(sm.redm[h][0], sm.redm[h][1]) : sm.redm[h][0];
     int ex = 0;
     if (mx > 0.0f) frexpf(mx, &ex);
-    sm.coefs[h][i] = i < nu ? sm.coefc[h][sm.ulist[i]] * ldexpf(1.0f, -ex) : 0.0f;
+    sm.coefs[h][i] = i + 1 < D ? sm.coefc[h][i + 1] * ldexpf(1.0f, -ex) : 0.0f;
     if (i == 0) sm.e2[h] = ldexpf(1.0f, ex);
   }
-  block_barrier();   // (not __syncthreads, which would wait for the loads just issued)
-  float ca[G], cb[G];   // coefficients of the two slots per head (0 past |U|)
+  block_barrier();
+  float ca[G], cb[G];   // coefficients of the two slots per head (0 outside U)
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     ca[h] = sm.coefs[h][as0];
     cb[h] = sm.coefs[h][as1];
   }
+  {
+    // later blocks read the union's channels only
+    const unsigned long long m0 = sm.umask[0], m1 = sm.umask[1];
+    auto member = [&](int ch) { return ((ch < 64 ? m0 >> ch : m1 >> (ch & 63)) & 1ull) != 0ull; };
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc)
+      if (!member(8 * lo + cc + 1)) kvo[cc] = kFar;
+    if (!member(as0 + 1)) ksv[0] = kFar;
+    if (!member(as1 + 1)) ksv[1] = kFar;
+  }
+  // the second block once the union is known (a smaller first burst of loads: the
+  // first blocks of every workgroup arrive sooner)
+  kissue(S1, t_begin + kBlock4, 1 < nbc0);
 
   auto kcommit = [&](KStage4<D> &S, KBlock4<D> &B, int p0) {
     {
