@@ -47,6 +47,8 @@
 // The capacity must be a multiple of 64 tokens (the key scales of a block are
 // then whole dwords of every scale row); other capacities use the general
 // decode kernel.
+#include <atomic>
+
 #include "dqk_internal.h"
 #include "dqk_wave.h"
 
@@ -253,7 +255,7 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
                                                                const float *__restrict__ qp,
                                                                const int32_t *__restrict__ sel,
                                                                int hq, int keep, float scale2,
-                                                               int nsplit, int bps,
+                                                               int nsplit, int bps, int ncu,
                                                                float *__restrict__ ws) {
   using L = Lay4<D>;
   constexpr int G = kG4;
@@ -289,10 +291,38 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
   }
   const int len = max(0, min(c.lengths[b], c.capacity));
   const int nblk_all = (len + kBlock4 - 1) / kBlock4;
-  // bps > 0: split s is blocks [s bps, (s + 1) bps) of the row; else the row's
-  // blocks are shared out evenly over the nsplit splits
-  const int blo = bps > 0 ? min(s * bps, nblk_all) : (int)(((long long)s * nblk_all) / nsplit);
-  const int bhi = bps > 0 ? min(blo + bps, nblk_all) : (int)(((long long)(s + 1) * nblk_all) / nsplit);
+  // bps > 0: split s is blocks [s bps, (s + 1) bps) of the row.  Else the row's
+  // blocks are shared out over the nsplit splits: evenly, or, when two workgroups
+  // share each compute unit (ncu > 0: the number of compute units, workgroup ids
+  // below it being the first on their unit), unevenly.  The first workgroup on a
+  // unit issues ahead of the second (older wavefronts win the issue arbitration)
+  // and would finish well before it, so the splits dispatched first take 9/8 of
+  // the average share, at most one chunk of nine blocks each, and the others share
+  // the rest evenly (with between 4 and about 8 blocks per split on average).
+  int blo, bhi;
+  {
+    const int fs = ncu > 0 ? min(nsplit, max(0, (ncu - unit + units - 1) / units)) : 0;   // first-slot splits
+    const int ss = nsplit - fs;
+    if (bps > 0) {
+      blo = min(s * bps, nblk_all);
+      bhi = min(blo + bps, nblk_all);
+    } else if (fs > 0 && ss > 0 && nblk_all >= 4 * nsplit && nblk_all <= 8 * nsplit + ss) {
+      // first-slot splits: cumulative 9/8 of the average, at most nine blocks each
+      const long long wt = 9LL * fs + 7LL * ss;
+      auto first = [&](int t) { return (int)min((9LL * nblk_all * t) / wt, 9LL * t); };
+      const int t1 = first(fs), rem = nblk_all - t1;
+      if (s < fs) {
+        blo = first(s);
+        bhi = first(s + 1);
+      } else {
+        blo = t1 + (int)(((long long)(s - fs) * rem) / ss);
+        bhi = t1 + (int)(((long long)(s - fs + 1) * rem) / ss);
+      }
+    } else {
+      blo = (int)(((long long)s * nblk_all) / nsplit);
+      bhi = (int)(((long long)(s + 1) * nblk_all) / nsplit);
+    }
+  }
   const int t_begin = blo * kBlock4;
   const int t_end = min(bhi * kBlock4, len);
   const int nb = bhi - blo;
@@ -951,6 +981,20 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
 
 }  // namespace
 
+int compute_units() {
+  static std::atomic<int> cache[64];   // per device: 0 = not yet queried
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    const int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 0;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 bool decode4_supported(const dqk_cache &c, int hq) {
   return c.capacity % 64 == 0 && hq % (c.num_kv_heads * kG4) == 0;
 }
@@ -965,12 +1009,19 @@ hipError_t launch_decode4(const dqk_cache &c, const float *q_prime, const int32_
   const int items = c.batch * c.num_kv_heads * nsplit;
   const int nsl = hq / (c.num_kv_heads * kG4);
   const dim3 grid((unsigned)(nsl > 1 ? (items + 7) / 8 * 8 * nsl : items)), block(kThreads4);
+  // uneven shares for two workgroups per compute unit (the library's own split of
+  // groups of four only)
+  int ncu = 0;
+  if (even && nsl == 1 && bps == 0) {
+    const int n = compute_units();
+    if (n > 0 && items > n && items <= 2 * n) ncu = n;
+  }
   if (c.head_dim == 64)
     hipLaunchKernelGGL((decode4_kernel<64>), grid, block, 0, s, c, q_prime, sel_idx, hq, keep, scale2, nsplit,
-                       bps, ws);
+                       bps, ncu, ws);
   else
     hipLaunchKernelGGL((decode4_kernel<128>), grid, block, 0, s, c, q_prime, sel_idx, hq, keep, scale2, nsplit,
-                       bps, ws);
+                       bps, ncu, ws);
   return hipGetLastError();
 }
 

@@ -85,6 +85,9 @@ __host__ __device__ __forceinline__ size_t unit_index(const dqk_cache &c, int b,
   return (size_t)b * c.num_kv_heads + g;
 }
 
+// Compute units of the current device (cached per device; 0 if the query fails).
+int compute_units();
+
 // Launchers (return the launch error, if any).
 hipError_t launch_append(const dqk_cache &c, const void *k_new, const void *v_new, bool bf16,
                          const float *bmat, const int32_t *n_new, int max_new, hipStream_t s);
