@@ -144,8 +144,15 @@ dqk_status dqk_decode_workspace_bytes(const dqk_cache *cache, int32_t hq,
  *   out[b][h] = sum_t softmax(z)_t v~_t        (T = 0 gives zeros)
  * where k~ is channel 0's fp16 value, the 2-bit value of complete groups, or the
  * exact tail.  Only the kept key channels' codes and scales are read from HBM.
- * The sequence is split into chunks of split_tokens (a positive multiple of 32;
- * 0 = the library's choice) reduced with an online-max combine.  Products run on the matrix cores with fp32 accumulation.
+ * The work is split along the sequence and the partial results are reduced with
+ * an online-max combine.  split_tokens (a positive multiple of 32, or 0 for the
+ * library's choice) fixes the number of splits, ceil(capacity / split_tokens).
+ * For groups of 4 or 8 query heads per KV head and a capacity that is a multiple of
+ * 64, the products run on the matrix cores with fp32 accumulation; there a multiple
+ * of 256 gives each split exactly its split_tokens tokens of every row, and other
+ * values share each row's current 256-token blocks out over the splits.  Otherwise
+ * split s covers tokens [s split_tokens, (s + 1) split_tokens).  The result does not
+ * depend on the split beyond fp32 rounding.
  * q_prime: [batch][hq][d] fp32; sel_idx: [batch][hq][keep] as produced by
  * dqk_select_channels; out: [batch][hq][d] fp32; workspace: device scratch of at
  * least dqk_decode_workspace_bytes (contents need no initialization). */
