@@ -303,21 +303,23 @@ def test_decode_workspace_reuse(orc):
     assert np.array_equal(fresh.view(np.uint32), out.cpu().numpy().view(np.uint32))
 
 
-def test_decode_ctx128k_sampled(orc):
+@pytest.mark.parametrize("ctx", [131072, 80000])
+def test_decode_ctx128k_sampled(orc, ctx):
     """The benchmark's workload at full size (batch 1, 32/8 heads, head_dim 128,
     131072 tokens, 40% sparsity) in its launch configuration (the default
-    split), at exactly 128K tokens, one past (a remainder split of one token)
-    and 33 past (a full key group and a tail token in the remainder split).
-    KV heads 0 and 5 are checked: the oracle decodes each from a one-KV-head
-    cache of that head's keys and values (the units are independent), built by
-    the same appends."""
-    wl = W.workload("ctx128k", steps=256)
+    split: 512 workgroups, two per compute unit, the first-dispatched ones taking
+    9/8 of the average share), at exactly 128K tokens, one past (one more block)
+    and 33 past (a full key group and a tail token in the last block); and the
+    same shape at 80000 tokens (about five blocks per split).  KV heads 0 and 5
+    are checked: the oracle decodes each from a one-KV-head cache of that head's
+    keys and values (the units are independent), built by the same appends."""
+    wl = W.workload("ctx128k", ctx=ctx, steps=256)
     ctx, sm = int(wl.ctx[0]), W.default_sm_scale(wl.d)
     extras = (0, 1, 33)
     n_all = ctx + extras[-1]
     a, b = W.transforms(wl)
     kscale = W.key_scales(wl)
-    say("ctx128k sampled: generating", n_all, "tokens x", wl.hkv, "KV heads")
+    say(f"ctx128k sampled ({ctx}): generating", n_all, "tokens x", wl.hkv, "KV heads")
     kb = np.zeros((1, wl.hkv, n_all, wl.d), dtype=np.uint16)
     vb = np.zeros_like(kb)
     sampled = {0: None, 5: None}
