@@ -28,7 +28,9 @@ SOURCES = {
     "dqk_step.hip": ["-ffp-contract=off"],
     "dqk_dequant.hip": ["-ffp-contract=off"],
     "dqk_decode.hip": ["-fno-honor-nans"],   # inputs are finite; only -inf is used
-    "dqk_decode4.hip": ["-fno-honor-nans"],
+    # the chunk loops (up to ten blocks, with a run-time exit) must unroll fully,
+    # or the chunk's logits would be indexed at run time and go to scratch memory
+    "dqk_decode4.hip": ["-fno-honor-nans", "-mllvm", "-unroll-max-upperbound=16"],
     "dqk_bf16.hip": [],
     "dqk_combine.hip": [],
     "dqk_probe.hip": [],

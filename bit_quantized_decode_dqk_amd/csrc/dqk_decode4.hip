@@ -12,7 +12,7 @@
 // last group, the exact tail.  Each head's logit uses only its own channels (its
 // coefficient is zero on the others).  Values are never pruned.
 //
-// Two passes per chunk of up to eight blocks (2048 tokens):
+// Two passes per chunk of up to ten blocks (2560 tokens):
 //  1. keys.  Every lane of the workgroup issues the same fixed set of buffer
 //     loads for a block (lanes without a part of it point past the plane, which
 //     returns zero and moves no bytes); two blocks are in flight in registers
@@ -65,10 +65,10 @@ constexpr int kThreads4 = 256;
 constexpr int kWaves4 = kThreads4 / 64;
 constexpr int kTile4 = 64;          // tokens per wavefront tile: two key groups
 constexpr int kBlock4 = kTile4 * kWaves4;   // tokens per workgroup block
-constexpr int kKsPerBlock = kBlock4 / kGroup;   // key groups per block
-constexpr int kChunk4 = 8;          // blocks per chunk: logits of a chunk stay in registers
-// a ninth block of a chunk is committed to LDS buffer 0 and uses value stage 2
-static_assert(kChunk4 % 2 == 0 && kChunk4 % 3 == 2, "ninth block stages");
+constexpr int kChunk4 = 10;         // blocks per chunk: logits of a chunk stay in registers
+// one block more than a chunk runs as one chunk: the extra block is committed to
+// LDS buffer kChunk4 & 1 and its values use stage kChunk4 % 3 (blocks alternate
+// over the two buffers and the value tiles over three stages)
 constexpr uint32_t kOneF16x2 = 0x3C003C00u;
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit elements, range-checked (gfx9)
 constexpr uint32_t kFar = 0x40000000u;   // offset past every plane: the load returns zero
@@ -146,9 +146,6 @@ struct VStage4 {
 
 __device__ __forceinline__ float h2f(uint32_t bits16) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
-}
-__device__ __forceinline__ uint16_t f2h(float x) {
-  return __builtin_bit_cast(uint16_t, (_Float16)x);
 }
 
 // c ? b : a on two values the compiler may not fold into an indexed load
@@ -296,9 +293,9 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
   // share each compute unit (ncu > 0: the number of compute units, workgroup ids
   // below it being the first on their unit), unevenly.  The first workgroup on a
   // unit issues ahead of the second (older wavefronts win the issue arbitration)
-  // and would finish well before it, so the splits dispatched first take 9/8 of
-  // the average share, at most one chunk of nine blocks each, and the others share
-  // the rest evenly (with between 4 and about 8 blocks per split on average).
+  // and would finish well before it, so the splits dispatched second take 7/8 of
+  // the average share and the first ones the rest, at most one chunk each (with
+  // between 4 and about 8 blocks per split on average).
   int blo, bhi;
   {
     const int fs = ncu > 0 ? min(nsplit, max(0, (ncu - unit + units - 1) / units)) : 0;   // first-slot splits
@@ -306,17 +303,19 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
     if (bps > 0) {
       blo = min(s * bps, nblk_all);
       bhi = min(blo + bps, nblk_all);
-    } else if (fs > 0 && ss > 0 && nblk_all >= 4 * nsplit && nblk_all <= 8 * nsplit + ss) {
-      // first-slot splits: cumulative 9/8 of the average, at most nine blocks each
+    } else if (fs > 0 && ss > 0 && nblk_all >= 4 * nsplit && nblk_all <= kChunk4 * fs + 8 * ss) {
+      // second-slot splits: 7/8 of the average share, rounded down, all the same
+      // (raised if the first-slot splits would need more than a chunk each); the
+      // first-slot splits share the rest evenly, at most one chunk each
       const long long wt = 9LL * fs + 7LL * ss;
-      auto first = [&](int t) { return (int)min((9LL * nblk_all * t) / wt, 9LL * t); };
-      const int t1 = first(fs), rem = nblk_all - t1;
+      const int a2 = max((int)((7LL * nblk_all) / wt), (nblk_all - kChunk4 * fs + ss - 1) / ss);
+      const int t1 = nblk_all - a2 * ss;
       if (s < fs) {
-        blo = first(s);
-        bhi = first(s + 1);
+        blo = (int)(((long long)t1 * s) / fs);
+        bhi = (int)(((long long)t1 * (s + 1)) / fs);
       } else {
-        blo = t1 + (int)(((long long)(s - fs) * rem) / ss);
-        bhi = t1 + (int)(((long long)(s - fs + 1) * rem) / ss);
+        blo = t1 + a2 * (s - fs);
+        bhi = blo + a2;
       }
     } else {
       blo = (int)(((long long)s * nblk_all) / nsplit);
@@ -596,7 +595,6 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) ez[hh][nt] = ldexpf(e, 25 - 2 * (3 + nt));
   }
-  u32x4 alog[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};   // logit A operands: zero in off-diagonal lanes
   u32x4 ones = {kOneF16x2, kOneF16x2, kOneF16x2, kOneF16x2};
 
   // Logits (log2 units) of this wavefront's tile of one block: z[hh][nt] for head
@@ -798,9 +796,9 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
     // a wavefront that is through with the previous chunk waits here until the
     // others have also read the key blocks of its last two blocks
     if (cb > 0) block_barrier();
-    // blocks in this chunk: up to eight, or nine when nine are left (the ninth
-    // takes the same steps after the first eight, with logits of its own), so
-    // that a share of just over eight blocks costs one block, not one chunk
+    // blocks in this chunk: up to kChunk4, or kChunk4 + 1 when that many are left
+    // (the extra block takes the same steps after the others, with logits of its
+    // own), so that a share of one block more costs one block, not one chunk
     const int nbc = nb - cb == kChunk4 + 1 ? kChunk4 + 1 : min(kChunk4, nb - cb);
     const int c_t0 = t_begin + kBlock4 * cb;         // first token of the chunk
     float zs[kChunk4][2][2];                         // this wavefront's logits of the chunk
@@ -835,9 +833,9 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
       kissue(S, p0 + 3 * kBlock4, i + 3 < nbc);
       block_barrier();
     }
-    float z9[2][2];   // the ninth block: committed to buffer 0 by the body of block 8
+    float z9[2][2];   // the extra block: committed to buffer kChunk4 & 1 by the last body
     if (nbc > kChunk4) {
-      logits(sm.kb[0], c_t0 + kBlock4 * kChunk4 + kTile4 * wave, z9);
+      logits(sm.kb[kChunk4 & 1], c_t0 + kBlock4 * kChunk4 + kTile4 * wave, z9);
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) zl[hh] = fmaxf(zl[hh], fmaxf(z9[hh][0], z9[hh][1]));
     }
@@ -900,9 +898,10 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
       if (tile0 < t_end) values(V, tile0, zs[i], mr);
       vissue(V, tile0 + 3 * kBlock4, i + 3 < nbc);
     }
-    if (nbc > kChunk4) {   // the ninth block's values are in stage V2 (8 % 3 == 2)
+    if (nbc > kChunk4) {   // the extra block's values are in stage kChunk4 % 3
       const int tile0 = c_t0 + kBlock4 * kChunk4 + kTile4 * wave;
-      if (tile0 < t_end) values(V2, tile0, z9, mr);
+      VStage4<D> &VX = kChunk4 % 3 == 0 ? V0 : kChunk4 % 3 == 1 ? V1 : V2;
+      if (tile0 < t_end) values(VX, tile0, z9, mr);
     }
     cb += nbc;
   }

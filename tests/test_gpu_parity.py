@@ -253,13 +253,14 @@ def test_decode_group4_many_blocks(orc, d, lens, cap):
     decode_case(orc, wl, sparsity=60, sm_mult=0.05, splits=(0,))
 
 
-def test_decode_group4_nine_block_chunks(orc):
-    """Shares of nine 256-token blocks run as one chunk of nine (a row of 2304
-    tokens, a ragged one of 2200 with its tail, one of 4300 split 8 + 9), with
-    one split per row, whole-block splits of nine blocks, and the default."""
-    wl = W.custom("g4-nine", 31, 3, 32, 8, 128, [2304, 2200, 4300], 4352, "bf16",
+def test_decode_group4_chunk_sizes(orc):
+    """Chunks of the dedicated kernel hold up to ten 256-token blocks, and a share
+    of eleven runs as one chunk with an extra block: rows of 2304, 2200 (ragged,
+    with its tail), 4300 and 5400 tokens, whole-block splits of 9, 10 and 11
+    blocks, one split per row (21 blocks: 10 + 11), and the default."""
+    wl = W.custom("g4-chunks", 31, 4, 32, 8, 128, [2304, 2200, 4300, 5400], 5440, "bf16",
                   log_uniform_key_scales=True)
-    decode_case(orc, wl, splits=(4352, 2304, 0))
+    decode_case(orc, wl, splits=(2304, 2560, 2816, 5440, 0))
 
 
 @pytest.mark.parametrize("hq,hkv,lens", [(4, 1, [3000, 1200, 64]), (12, 3, [2500]),
