@@ -306,16 +306,19 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
     } else if (fs > 0 && ss > 0 && nblk_all >= 4 * nsplit && nblk_all <= kChunk4 * fs + 8 * ss) {
       // second-slot splits: 7/8 of the average share, rounded down, all the same
       // (raised if the first-slot splits would need more than a chunk each); the
-      // first-slot splits share the rest evenly, at most one chunk each
+      // first-slot splits share the rest evenly, at most one chunk each.  The last
+      // split, which also works out the exact logits of an unfinished last key
+      // group, takes one block less when there is one.
+      const int cut = len % kGroup != 0 ? 1 : 0;
       const long long wt = 9LL * fs + 7LL * ss;
-      const int a2 = max((int)((7LL * nblk_all) / wt), (nblk_all - kChunk4 * fs + ss - 1) / ss);
-      const int t1 = nblk_all - a2 * ss;
+      const int a2 = max((int)((7LL * nblk_all) / wt), (nblk_all + cut - kChunk4 * fs + ss - 1) / ss);
+      const int t1 = nblk_all - a2 * ss + cut;
       if (s < fs) {
         blo = (int)(((long long)t1 * s) / fs);
         bhi = (int)(((long long)t1 * (s + 1)) / fs);
       } else {
         blo = t1 + a2 * (s - fs);
-        bhi = blo + a2;
+        bhi = s == nsplit - 1 ? nblk_all : blo + a2;
       }
     } else {
       blo = (int)(((long long)s * nblk_all) / nsplit);
