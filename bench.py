@@ -88,12 +88,27 @@ KERNEL_SOURCES = ("bit_quantized_decode_dqk_amd/csrc/dqk_decode.hip",
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_ctx128k_traffic.txt")
 
 
-def kernel_source_hash() -> str:
+def kernel_code(text: str) -> str:
+    """C/C++ source with comments removed and whitespace collapsed: what the
+    compiler sees of it (string literals in these sources hold no comment marks)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
+def kernel_source_hash(root: str = ROOT, read=None) -> str:
+    """Hash of the decode kernels' code (comments and layout ignored), stamped into the
+    counter summary so that a summary taken on other code is not used."""
     import hashlib
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        if read is None:
+            with open(os.path.join(root, rel), encoding="utf-8") as f:
+                text = f.read()
+        else:
+            text = read(rel)
+        h.update(kernel_code(text).encode())
     return h.hexdigest()[:16]
 
 

@@ -5,11 +5,12 @@
 // Dual-QK (arXiv abstract; tech.dede.sh summary, "Throughput on SGLang"): keys
 // and values are stored in 2 bits and the key channels a query head does not
 // keep are never read, which is where the decode speedup comes from.  One
-// workgroup serves the four query heads of one KV head over an equal share of
-// the sequence's 256-token blocks; only the union U of the group's kept key
-// channels is read (their 2-bit rows are channel-major, so a dropped channel
-// costs no bytes), together with channel 0's fp16 row and, for the unfinished
-// last group, the exact tail.  Each head's logit uses only its own channels (its
+// workgroup serves the four query heads of one KV head over a share of the
+// sequence's 256-token blocks; only the union U of the group's kept key channels
+// is read (their 2-bit rows are channel-major, so a dropped channel costs no
+// bytes; the workgroup's first block, issued before U is known, reads every
+// channel), together with channel 0's fp16 row and, for the unfinished last
+// group, the exact tail.  Each head's logit uses only its own channels (its
 // coefficient is zero on the others).  Values are never pruned.
 //
 // Two passes per chunk of up to ten blocks (2560 tokens):
