@@ -516,6 +516,10 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
     ca[h] = sm.coefs[h][as0];
     cb[h] = sm.coefs[h][as1];
   }
+  // Key scales of the A-building slots outside U count as zero: the first block
+  // read them (their coefficients are zero, but a scale that is not finite would
+  // still poison the products), later blocks do not read them.
+  uint32_t ksm[2];
   {
     // later blocks read the union's channels only
     const unsigned long long m0 = sm.umask[0], m1 = sm.umask[1];
@@ -523,8 +527,10 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
 #pragma unroll
     for (int cc = 0; cc < 8; ++cc)
       if (!member(8 * lo + cc + 1)) kvo[cc] = kFar;
-    if (!member(as0 + 1)) ksv[0] = kFar;
-    if (!member(as1 + 1)) ksv[1] = kFar;
+    ksm[0] = member(as0 + 1) ? 0xffffffffu : 0u;
+    ksm[1] = member(as1 + 1) ? 0xffffffffu : 0u;
+    if (!ksm[0]) ksv[0] = kFar;
+    if (!ksm[1]) ksv[1] = kFar;
   }
   // the second block once the union is known (a smaller first burst of loads: the
   // first blocks of every workgroup arrive sooner)
@@ -553,7 +559,7 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
     // logit A operands: key scales of a key group past the coded range (the exact
     // tail or beyond) count as zero.  High part = fp16 of the product, low part =
     // fp16 of what the high part leaves out (about 22 significant bits together).
-    uint32_t v0 = S.ks[0], v1 = S.ks[1];
+    uint32_t v0 = S.ks[0] & ksm[0], v1 = S.ks[1] & ksm[1];
     if (p0 + kBlock4 > code_end) {   // workgroup-uniform
       const int g0 = p0 / kGroup + 2 * agp;
       const uint32_t km = (g0 * kGroup < code_end ? 0xffffu : 0u) | ((g0 + 1) * kGroup < code_end ? 0xffff0000u : 0u);

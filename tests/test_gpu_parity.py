@@ -464,10 +464,15 @@ def test_step_graph_replay_matches_eager(orc):
         assert np.array_equal(out.cpu().numpy().view(np.uint32), out_e.cpu().numpy().view(np.uint32)), r
 
 
-def test_decode_poisoned_dropped_channels(orc):
+@pytest.mark.parametrize("hq,cap", [(32, 1504), (32, 1536), (64, 1536)])
+def test_decode_poisoned_dropped_channels(orc, hq, cap):
     """Codes and scales of channels no head of the group keeps are overwritten
-    with 0xFF / fp16 NaN: the output is bitwise unchanged, so they are never used."""
-    wl = W.workload("gqa8k", batch=2, ctx=1500)
+    with 0xFF / fp16 NaN: the output is bitwise unchanged, so their contents are
+    never used (the general kernel, capacity 1504, does not read them; the
+    matrix-core kernel, capacity 1536, groups of 4 and 8, reads them only in a
+    workgroup's first block and gives them zero weight)."""
+    wl = W.custom(f"poison{hq}-{cap}", 2, 2, hq, 8, 128, [1500, 1500], cap, "bf16",
+                  log_uniform_key_scales=True)
     g, a, b, k, v = build_gpu(wl)
     keep = orc.keep_count(wl.d, 60)
     qp, idx = gpu_queries(wl, W.queries(wl), a, keep)
