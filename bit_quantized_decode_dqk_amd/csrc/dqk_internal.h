@@ -30,18 +30,20 @@ inline int balanced_decode_split(int capacity, int workgroups) {
 }
 
 // Default split of the matrix-core decode.  When the capacity alone gives more
-// than 16 blocks of 256 tokens per resident workgroup slot (512), fixed splits of
-// 16 whole blocks: work items then outnumber the slots several times and the
-// dispatcher evens out rows of different lengths.  Otherwise the balanced split
-// count above, each split taking an equal share of its row's current blocks
+// than kFixedSplitBlocks blocks of 256 tokens per resident workgroup slot (512),
+// fixed splits of that many whole blocks (two chunks of the kernel: ten blocks,
+// then ten and an extra one): work items then outnumber the slots several times
+// and the dispatcher evens out rows of different lengths.  Otherwise the balanced
+// split count above, each split taking an equal share of its row's current blocks
 // (even = true).
+constexpr int kFixedSplitBlocks = 21;
 struct DecodeSplit {
   int split;
   bool even;
 };
 inline DecodeSplit matrix_decode_split(int capacity, int workgroups) {
   const long long blocks = (long long)workgroups * ((capacity + 255) / 256);
-  if (blocks > 16LL * 512) return {16 * 256, false};
+  if (blocks > (long long)kFixedSplitBlocks * 512) return {kFixedSplitBlocks * 256, false};
   return {balanced_decode_split(capacity, workgroups), true};
 }
 

@@ -83,7 +83,7 @@ def test_default_split_for_groups_of_four():
     """Default split of the four-head decode, read back through the workspace
     size (one partial of G heads x (d + 4) floats per split and (row, KV head)):
     about 512 workgroups (two per compute unit on 256), at least 256 tokens of
-    capacity each, unless the capacity alone gives more than 16 blocks per slot.
+    capacity each, unless the capacity alone gives more than 21 blocks per slot.
     Groups of eight run as two four-head workgroups per split."""
     L = M.lib()
     out = C.c_size_t(0)
@@ -95,11 +95,12 @@ def test_default_split_for_groups_of_four():
         assert out.value % per == 0
         return out.value // per
 
-    # more than 16 blocks per slot of 512 from the capacity alone: whole-block
-    # splits of 16 blocks (4096 tokens)
-    assert splits(16, 8, 65536, 8) == 16       # 128 units x 2 slices x 256 blocks
-    assert splits(8, 8, 131072) == 32          # 64 units x 512 blocks
+    # more than 21 blocks per slot of 512 from the capacity alone: whole-block
+    # splits of 21 blocks (5376 tokens)
+    assert splits(16, 8, 65536, 8) == 13       # 128 units x 2 slices x 256 blocks
+    assert splits(8, 8, 131072) == 25          # 64 units x 512 blocks
     assert splits(8, 8, 32768) == 8            # 64 x 128 blocks = 8192: balanced, 8 per unit
+    assert splits(8, 8, 32768 + 192) == 8      # 64 x 129 blocks: still balanced
     assert splits(1, 8, 131072, 8) == 32
     assert splits(1, 1, 4096, 8) == 16
 

@@ -363,8 +363,8 @@ def test_decode_ragged64k_sampled(orc):
     """The ragged group-of-eight workload at full size (batch 16, 64/8 heads,
     head_dim 128, rows of 20K..62K tokens in a 64K capacity, 40% sparsity,
     Student-t queries) in its launch configuration: the default split, here
-    whole-block splits of 16 blocks with two four-head workgroups per split (and
-    an equal-share split for comparison).  Three (row, KV head) units are checked
+    whole-block splits of 21 blocks (chunks of 10 and 10 + 1) with two four-head
+    workgroups per split (and 16-block and equal-share splits for comparison).  Three (row, KV head) units are checked
     against the oracle: the longest row, the shortest and a middle one.  They hold
     the workload's own keys and values; the other units hold normal draws of the
     same channel scales (the units are independent)."""
@@ -407,14 +407,14 @@ def test_decode_ragged64k_sampled(orc):
         assert np.array_equal(idx_np[bb:bb + 1, hs], idxo), (bb, g)
         refs[(bb, g)] = oc.decode(qpo, idxo, sm)
     outs = {}
-    for sp in (0, 4096, 8224):
+    for sp in (0, 5376, 4096, 8224):
         outs[sp] = out = M.decode_attention(cache, qp, idx, sm, split_tokens=sp).cpu().numpy()
         for (bb, g), ref in refs.items():
             err = rel_err(out[bb:bb + 1, 8 * g:8 * g + 8], ref)
             say(f"  split {sp}, row {bb}, KV head {g}: max rel err {err:.3e}")
             assert err <= REL_TOL, (sp, bb, g, err)
-    # the default is whole-block splits of 4096 tokens here: the same launch
-    assert np.array_equal(outs[0].view(np.uint32), outs[4096].view(np.uint32))
+    # the default is whole-block splits of 5376 tokens here: the same launch
+    assert np.array_equal(outs[0].view(np.uint32), outs[5376].view(np.uint32))
 
 
 def test_step_graph_replay_matches_eager(orc):
