@@ -201,6 +201,8 @@ def append_select(cache: Cache, k_new, v_new, bmat, n_new, q, amat, keep: int, q
 
 
 def decode_workspace_bytes(cache: Cache, hq: int, split_tokens: int = 0) -> int:
+    """Bytes of device workspace dqk_decode_attention needs for this cache shape, hq
+    query heads and split length (0: the library's choice), as dqk.h defines it."""
     out = C.c_size_t(0)
     s = cache.struct()
     _check(lib().dqk_decode_workspace_bytes(C.byref(s), hq, split_tokens, C.byref(out)),
@@ -210,6 +212,10 @@ def decode_workspace_bytes(cache: Cache, hq: int, split_tokens: int = 0) -> int:
 
 def decode_attention(cache: Cache, q_prime, sel_idx, sm_scale: float, split_tokens: int = 0,
                      out=None, workspace=None, stream=None):
+    """Pruned 2-bit decode attention (dqk_decode_attention): q_prime [batch][hq][d] fp32
+    and sel_idx [batch][hq][keep] int32 as dqk_select_channels leaves them; returns out
+    [batch][hq][d] fp32 (allocated when not given).  The workspace, if given, holds at
+    least decode_workspace_bytes(...) bytes and needs no initialization."""
     torch = _torch()
     batch, hq, d = q_prime.shape
     keep = int(sel_idx.shape[-1])
