@@ -113,6 +113,8 @@ def keep_for_sparsity(head_dim: int, sparsity_pct: int) -> int:
 
 
 def cache_plane_bytes(batch: int, hkv: int, d: int, cap: int):
+    """Bytes of each of the cache's seven planes (k_codes, k_scales, k_ch0, k_tail,
+    v_codes, v_scales, lengths) for this shape; a host query, no GPU needed."""
     out = (C.c_size_t * 7)()
     _check(lib().dqk_cache_plane_bytes(batch, hkv, d, cap, out), "dqk_cache_plane_bytes")
     return list(out)
@@ -234,6 +236,8 @@ def decode_attention(cache: Cache, q_prime, sel_idx, sm_scale: float, split_toke
 
 
 def dequant_reference(cache: Cache, stream=None):
+    """Dense dequantized keys and values [batch][hkv][capacity][d] fp32 (zero past each
+    row's length): a checking and inspection aid, not on the decode path."""
     torch = _torch()
     shape = (cache.batch, cache.hkv, cache.cap, cache.d)
     k = torch.empty(shape, dtype=torch.float32, device=cache.k_codes.device)
@@ -245,6 +249,7 @@ def dequant_reference(cache: Cache, stream=None):
 
 
 def bf16_decode_workspace_bytes(batch, hq, hkv, d, ld_t, split_tokens=0) -> int:
+    """Workspace bytes of the unpruned bf16 comparator for this shape and split."""
     out = C.c_size_t(0)
     _check(lib().dqk_bf16_decode_workspace_bytes(batch, hq, hkv, d, ld_t, split_tokens,
                                                  C.byref(out)), "dqk_bf16_decode_workspace_bytes")
@@ -253,7 +258,9 @@ def bf16_decode_workspace_bytes(batch, hq, hkv, d, ld_t, split_tokens=0) -> int:
 
 def bf16_decode_attention(q, k, v, lengths, sm_scale: float, split_tokens: int = 0, out=None,
                           workspace=None, stream=None):
-    """q [batch][hq][d] bf16; k/v [batch][hkv][ld_t][d] bf16; lengths [batch] int32."""
+    """The unpruned bf16 comparator: plain decode attention over raw keys and values.
+    q [batch][hq][d] bf16; k/v [batch][hkv][ld_t][d] bf16; lengths [batch] int32;
+    returns out [batch][hq][d] fp32."""
     torch = _torch()
     batch, hq, d = q.shape
     hkv, ld_t = int(k.shape[1]), int(k.shape[2])
@@ -275,6 +282,8 @@ def bf16_decode_attention(q, k, v, lengths, sm_scale: float, split_tokens: int =
 
 
 def debug_f16_from_f32(x, stream=None):
+    """The device's fp32 -> fp16 conversion (the one every stored scale and channel-0
+    key uses), element-wise; returns the fp16 bit patterns as int16."""
     torch = _torch()
     out = torch.empty(x.shape, dtype=torch.int16, device=x.device)   # fp16 bits
     _check(lib().dqk_debug_f16_from_f32(_ptr(x), _ptr(out), x.numel(), _stream(stream)),
