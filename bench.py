@@ -300,6 +300,18 @@ def main():
             getattr(c, name).copy_(t)
     torch.cuda.synchronize()
     log(f"{args.copies} cache copies of {caches[0].nbytes() / 1e6:.1f} MB built")
+    # input statistics: condition number of the query transforms, and the largest
+    # transformed key magnitudes (all channels, and channel 0 alone), over the prefill
+    cond_a = float(max(np.linalg.cond(a[g].astype(np.float64)) for g in range(wl.hkv)))
+    kmax, k0max = 0.0, 0.0
+    for g in range(wl.hkv):
+        kp = torch.matmul(k_d[:, g].float(), b_d[g])      # k' = k B_g, fp32
+        kmax = max(kmax, float(kp.abs().max()))
+        k0max = max(k0max, float(kp[..., 0].abs().max()))
+        del kp
+    inputs = {"cond_A_max": round(cond_a, 1), "max_abs_k_prime": round(kmax, 1),
+              "max_abs_k_prime_ch0": round(k0max, 1)}
+    log(f"inputs: {inputs}")
 
     nstep = args.warmup + args.steps
     # step inputs: the eager steps, then the steps captured in the graph (replayed twice)
@@ -434,7 +446,7 @@ def main():
                                f"INT2 K/V groups of 32, {args.sparsity}% query-channel sparsity, "
                                "step = append 1 token + select + decode",
                    "global_batch": wl.batch, "seq_len": ctx, "parallelism": "none (1 GPU)",
-                   "keep": keep, "cache_copies": args.copies,
+                   "keep": keep, "cache_copies": args.copies, "inputs": inputs,
                    "timing": ("the K steps captured once as a HIP graph and replayed "
                               "(untimed replay first); the eager loop is under 'eager'"
                               if args.graph else "eager launches")},
