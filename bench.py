@@ -462,6 +462,10 @@ def main():
         result["eager"] = eager
     if extras:
         result["extras"] = extras
+        read_peak = extras.get("stream_peak", {}).get("read_GB/s")
+        if read_peak:   # the practical ceiling: a plain streaming read measured in this process
+            result["roofline"]["measured_read_peak"] = read_peak
+            result["roofline"]["frac_of_measured_read_peak"] = round(roof_gbs / read_peak, 4)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         result["cpu_baseline"] = cpu_baseline(wl, a, b, keep, sm)
