@@ -178,11 +178,19 @@ __device__ __forceinline__ void append_block(int block, const dqk_cache &c, cons
   const int unit = block / blocks_per_unit;
   const int bi = block % blocks_per_unit;
   const int b = unit / c.num_kv_heads, g = unit % c.num_kv_heads;
-  // column tid % D of B_g, in flight together with the length
+  // column tid % D of B_g, in flight together with the length.  Only threads
+  // whose token slot tid / D can hold a new token use it (a group gets at most
+  // max_new of them); the others load nothing, which halves the workgroup's
+  // reads of B_g for one-token appends.
   float bcol[D];
-  const float *bp = bmat + (size_t)g * D * D + threadIdx.x % D;
+  if ((int)(threadIdx.x / D) < max_new) {
+    const float *bp = bmat + (size_t)g * D * D + threadIdx.x % D;
 #pragma unroll
-  for (int i = 0; i < D; ++i) bcol[i] = bp[(size_t)i * D];
+    for (int i = 0; i < D; ++i) bcol[i] = bp[(size_t)i * D];
+  } else {
+#pragma unroll
+    for (int i = 0; i < D; ++i) bcol[i] = 0.0f;
+  }
   const int L = c.lengths[b];
   const int n = max(0, min(min(n_new[b], max_new), c.capacity - L));
   if (n <= 0) return;

@@ -16,7 +16,7 @@ __global__ __launch_bounds__(selb::kThreads) void select_kernel(const void *q,
 template <int D, int G>
 void launch_g(const void *q, bool bf16, const float *amat, int batch, int hq, int hkv, int keep,
               float *q_prime, int32_t *sel_idx, hipStream_t s) {
-  const dim3 grid((unsigned)(batch * hkv));
+  const dim3 grid((unsigned)(batch * hkv * selb::blocks_per_unit<D, G>()));
   if (bf16)
     hipLaunchKernelGGL((select_kernel<D, G, true>), grid, dim3(selb::kThreads), 0, s, q, amat, hq, hkv, keep, q_prime, sel_idx);
   else

@@ -9,11 +9,11 @@
 // |q'|, equal magnitudes going to the lower index; the kept set is written in
 // ascending order.
 //
-// One workgroup of 256 lanes per (batch row, KV head) serves the group's query
-// heads: every output is an fp32 FMA chain over input channels in ascending
-// order (bit-reproducible); then each wavefront finds one head's exact top-k by
-// a bitwise search over the magnitudes' bit patterns with ballots, and ballot
-// prefixes give each kept channel its ascending slot.  Built with
+// A workgroup of 256 lanes serves one query head (two for head_dim 64): every
+// output is an fp32 FMA chain over input channels in ascending order
+// (bit-reproducible); then one wavefront per head finds the head's exact top-k
+// by a bitwise search over the magnitudes' bit patterns with ballots, and
+// ballot prefixes give each kept channel its ascending slot.  Built with
 // -ffp-contract=off.
 #pragma once
 #include "dqk_internal.h"
@@ -68,80 +68,72 @@ __device__ void select_one_head(const float *mag, int keep, int32_t *idx) {
   if (s1) idx[popc(m0) + popc(m1 & below)] = c1;
 }
 
-// One workgroup per (batch row, KV head); the G query heads of the group share
-// A_g.  Thread j forms q'_c for column c = j % D of the heads of its thread
-// group j / D (G heads spread over kThreads / D groups); each wavefront then
-// selects for every fourth head.
+// Heads per workgroup: one thread group of D lanes per head, and at most half
+// of the workgroup's lanes, so that a workgroup reads A_g (D*D floats) at most
+// twice: for D = 128 one head per workgroup.  The G heads of a KV head
+// therefore take several workgroups, each on its own CU: the per-CU load of A_g
+// sets the length of the setup.
+template <int D>
+constexpr int heads_per_block() { return kThreads / D >= 4 ? kThreads / D / 2 : 1; }
+
+template <int D, int G>
+constexpr int blocks_per_unit() { return (G + heads_per_block<D>() - 1) / heads_per_block<D>(); }
+
+// Workgroup BLOCK serves (batch row, KV head) BLOCK / blocks_per_unit and, of
+// that group's query heads, the heads_per_block heads from (BLOCK mod
+// blocks_per_unit) * heads_per_block on.  Thread j of thread group t (j / D)
+// forms q'_c for column c = j % D of head t; each of the first waves then
+// selects one head.
 template <int D, int G, bool BF16>
 __device__ __forceinline__ void select_block(int block, const void *q,
                                              const float *__restrict__ amat, int hq, int hkv,
                                              int keep, float *q_prime, int32_t *sel_idx) {
-  __shared__ __attribute__((aligned(16))) float qs[G][D];
-  __shared__ float mag[G][D];
-  const int b = block / hkv, g = block % hkv;
-  const size_t row0 = (size_t)b * hq + (size_t)g * G;
+  constexpr int HPB = heads_per_block<D>(), NSUB = blocks_per_unit<D, G>();
+  static_assert(HPB * D <= kThreads && HPB * 64 <= kThreads, "one thread group and one wave per head");
+  __shared__ float qs[HPB][D];
+  __shared__ float mag[HPB][D];
+  const int unit = block / NSUB, h0 = (block % NSUB) * HPB;
+  const int b = unit / hkv, g = unit % hkv;
+  const size_t row0 = (size_t)b * hq + (size_t)g * G + h0;
   const int j = threadIdx.x, wave = j >> 6;
-  // The query rows and lane j's whole column of A_g are loaded together: the
-  // setup is one round trip.
-  constexpr int QJ = (G * D + kThreads - 1) / kThreads;
-  float qv[QJ];
-#pragma unroll
-  for (int k = 0; k < QJ; ++k) {
-    const int e = min(j + kThreads * k, G * D - 1);   // unconditional loads (no branch between them)
-    if constexpr (BF16)
-      qv[k] = bf16_value(static_cast<const uint16_t *>(q)[row0 * D + e]);
-    else
-      qv[k] = static_cast<const float *>(q)[row0 * D + e];
-  }
-  constexpr int NGRP = kThreads / D;            // thread groups (one per D threads)
-  constexpr int HPT = (G + NGRP - 1) / NGRP;    // heads per thread
-  const int col = j % D, grp = j / D;           // grp is uniform in a wavefront
+  const int col = j % D, grp = j / D;                 // grp is uniform in a wavefront
+  const int nh = min(HPB, G - h0);                    // heads of this workgroup
+  // The query value and the lane's whole column of A_g are loaded together:
+  // the setup is one round trip.  Thread groups without a head load nothing.
   float a[D];
-  const float *acol = amat + (size_t)g * D * D + col;
+  if (grp < nh) {
+    const size_t e = (row0 + grp) * D + col;
+    float qv;
+    if constexpr (BF16)
+      qv = bf16_value(static_cast<const uint16_t *>(q)[e]);
+    else
+      qv = static_cast<const float *>(q)[e];
+    const float *acol = amat + (size_t)g * D * D + col;
 #pragma unroll
-  for (int r = 0; r < D; ++r) a[r] = acol[(size_t)r * D];
+    for (int r = 0; r < D; ++r) a[r] = acol[(size_t)r * D];
+    qs[grp][col] = qv;
+    // A's column is used here so that its loads are issued before the
+    // barrier, together with the query load (A is read-only: the compiler
+    // would otherwise move them past the barrier, a second round trip)
 #pragma unroll
-  for (int k = 0; k < QJ; ++k) {   // clamped like the loads: the last element may be written twice
-    const int e = min(j + kThreads * k, G * D - 1);
-    qs[e / D][e % D] = qv[k];
+    for (int r = 0; r < D; ++r) asm volatile("" ::"v"(a[r]));
   }
-  // A's column is used here so that its loads are issued before the barrier,
-  // together with the query loads (A is read-only: the compiler would otherwise
-  // move them past the barrier, a second round trip)
-#pragma unroll
-  for (int r = 0; r < D; ++r) asm volatile("" ::"v"(a[r]));
   __syncthreads();
-  // thread group GRP's heads as compile-time rows of qs (a runtime head index
-  // makes the compiler hoist every LDS read of the chain at once)
+  // the thread group's row of qs at a compile-time index (a runtime row makes
+  // the compiler hoist every LDS read of the chain at once)
   auto chain = [&](auto grp_c) {
     constexpr int GRP = decltype(grp_c)::value;
-    float acc[HPT];
+    float acc = 0.0f;
 #pragma unroll
-    for (int i = 0; i < HPT; ++i) acc[i] = 0.0f;
-#pragma unroll
-    for (int r = 0; r < D; ++r)
-#pragma unroll
-      for (int i = 0; i < HPT; ++i) {
-        acc[i] = __builtin_fmaf(qs[min(GRP * HPT + i, G - 1)][r], a[r], acc[i]);
-      }
-#pragma unroll
-    for (int i = 0; i < HPT; ++i) {
-      const int h = GRP * HPT + i;
-      if (h < G) {
-        q_prime[(row0 + h) * D + col] = acc[i];
-        mag[h][col] = fabsf(acc[i]);
-      }
-    }
+    for (int r = 0; r < D; ++r) acc = __builtin_fmaf(qs[GRP][r], a[r], acc);
+    q_prime[(row0 + GRP) * D + col] = acc;
+    mag[GRP][col] = fabsf(acc);
   };
-  static_assert(NGRP <= 4, "thread groups");
-  switch (grp) {   // uniform in a wavefront
-    case 0: chain(std::integral_constant<int, 0>{}); break;
-    case 1: if constexpr (NGRP > 1) chain(std::integral_constant<int, 1>{}); break;
-    case 2: if constexpr (NGRP > 2) chain(std::integral_constant<int, 2>{}); break;
-    default: if constexpr (NGRP > 3) chain(std::integral_constant<int, 3>{}); break;
-  }
+  static_assert(HPB <= 2, "thread groups with a head");
+  if (grp == 0 && nh > 0) chain(std::integral_constant<int, 0>{});
+  else if constexpr (HPB > 1) { if (grp == 1 && nh > 1) chain(std::integral_constant<int, 1>{}); }
   __syncthreads();
-  for (int h = wave; h < G; h += kThreads / 64) select_one_head<D>(mag[h], keep, sel_idx + (row0 + h) * keep);
+  if (wave < nh) select_one_head<D>(mag[wave], keep, sel_idx + (row0 + wave) * keep);
 }
 
 }  // namespace selb

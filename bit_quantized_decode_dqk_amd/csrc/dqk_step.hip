@@ -2,7 +2,7 @@
 // append and the query's channel selection (Dual-QK: tech.dede.sh summary,
 // "Paired transforms instead of shared rotation" -- keys and queries go through
 // their own transforms; arXiv abstract -- INT2 cache, dynamic channel pruning).
-// The selection workgroups (one per (row, KV head); they take longer) come first
+// The selection workgroups (one per query head; they take longer) come first
 // in the grid, the append workgroups after them; each runs the same body as in
 // its own kernel (the append workgroups commit the lengths).  Built with
 // -ffp-contract=off.
@@ -19,7 +19,7 @@ __global__ __launch_bounds__(appb::kThreads) void append_select_kernel(
     dqk_cache c, const void *k_new, const void *v_new, const float *__restrict__ bmat,
     const int32_t *__restrict__ n_new, int max_new, int blocks_per_unit, const void *q,
     const float *__restrict__ amat, int hq, int keep, float *q_prime, int32_t *sel_idx) {
-  const int sel_blocks = c.batch * c.num_kv_heads;
+  const int sel_blocks = c.batch * c.num_kv_heads * selb::blocks_per_unit<D, G>();
   if ((int)blockIdx.x < sel_blocks)   // workgroup-uniform
     selb::select_block<D, G, BF16>(blockIdx.x, q, amat, hq, c.num_kv_heads, keep, q_prime, sel_idx);
   else
@@ -34,7 +34,8 @@ void launch_g(const dqk_cache &c, const void *k_new, const void *v_new, bool bf1
               hipStream_t s) {
   const int units = c.batch * c.num_kv_heads;
   const int per_unit = (max_new + kGroup - 1) / kGroup + 1;  // as in the append launch
-  const dim3 grid((unsigned)(units + units * per_unit)), block(appb::kThreads);
+  const dim3 grid((unsigned)(units * selb::blocks_per_unit<D, G>() + units * per_unit)),
+      block(appb::kThreads);
   if (bf16)
     hipLaunchKernelGGL((append_select_kernel<D, G, true>), grid, block, 0, s, c, k_new, v_new, bmat,
                        n_new, max_new, per_unit, q, amat, hq, keep, q_prime, sel_idx);
