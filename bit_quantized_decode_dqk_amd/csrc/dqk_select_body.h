@@ -11,9 +11,10 @@
 //
 // A workgroup of 256 lanes serves one query head (two for head_dim 64): every
 // output is an fp32 FMA chain over input channels in ascending order
-// (bit-reproducible); then one wavefront per head finds the head's exact top-k
-// by a bitwise search over the magnitudes' bit patterns with ballots, and
-// ballot prefixes give each kept channel its ascending slot.  Built with
+// (bit-reproducible); then every channel's rank in the order (|q'| descending,
+// index ascending) is counted exactly -- the workgroup's wavefronts each
+// compare against a slice of the channels -- the channels of rank below keep-1
+// are kept, and ballot prefixes give each kept channel its ascending slot.  Built with
 // -ffp-contract=off.
 #pragma once
 #include "dqk_internal.h"
@@ -27,45 +28,16 @@ constexpr int kThreads = 256;
 
 __device__ __forceinline__ int popc(unsigned long long m) { return __popcll(m); }
 
-// Exact top-(k) of one head's |q'| over channels 1..D-1 inside one wavefront:
-// lane l holds channels l and l+64.  Magnitudes are non-negative floats, so
-// their bit patterns order like the values; a bitwise search from the top bit
-// finds the k-th largest pattern T, channels above T are kept, and of the
-// channels equal to T the lowest indices are kept.  The search stops early once
-// exactly k patterns are at or above the prefix found so far: that set is then
-// the answer (the full search would end on a T with the same set).  Writes
-// idx[0..keep) ascending.
+// Order key of channel c with magnitude |q'_c|: non-negative floats order like
+// their bit patterns, and the low bits (D-1-c) put the lower index first among
+// equal magnitudes, so every channel's key is distinct and the larger key
+// comes first.  Channel 0 gets key 0: it is kept apart from the competition
+// and no key counted against another is ever 0 (a key is counted when it is
+// larger).
 template <int D>
-__device__ void select_one_head(const float *mag, int keep, int32_t *idx) {
-  const int lane = threadIdx.x & 63;
-  const unsigned long long below = (1ull << lane) - 1ull;
-  const int c0 = lane, c1 = lane + 64;
-  const bool v0 = c0 >= 1 && c0 < D, v1 = c1 < D;
-  const uint32_t k0 = v0 ? __float_as_uint(mag[c0]) : 0u;
-  const uint32_t k1 = v1 ? __float_as_uint(mag[c1]) : 0u;
-  const int want = keep - 1;             // channels to keep besides channel 0
-  bool s0 = false, s1 = false;
-  if (want > 0) {
-    uint32_t t = 0;
-    for (int bit = 30; bit >= 0; --bit) {
-      const uint32_t cand = t | (1u << bit);
-      const int n = popc(__ballot(v0 && k0 >= cand)) + popc(__ballot(v1 && k1 >= cand));
-      if (n >= want) {
-        t = cand;
-        if (n == want) break;
-      }
-    }
-    const unsigned long long g0 = __ballot(v0 && k0 > t), g1 = __ballot(v1 && k1 > t);
-    const unsigned long long e0 = __ballot(v0 && k0 == t), e1 = __ballot(v1 && k1 == t);
-    const int need = want - popc(g0) - popc(g1);   // equal channels still to take
-    const int r0 = popc(e0 & below), r1 = popc(e0) + popc(e1 & below);
-    s0 = (v0 && k0 > t) || (v0 && k0 == t && r0 < need);
-    s1 = (v1 && k1 > t) || (v1 && k1 == t && r1 < need);
-  }
-  if (c0 == 0) s0 = true;                // the protected channel
-  const unsigned long long m0 = __ballot(s0), m1 = __ballot(s1);
-  if (s0) idx[popc(m0 & below)] = c0;
-  if (s1) idx[popc(m0) + popc(m1 & below)] = c1;
+__device__ __forceinline__ uint64_t order_key(float x, int c) {
+  static_assert(D <= 128, "index field of 7 bits");
+  return c == 0 ? 0ull : ((uint64_t)__float_as_uint(fabsf(x)) << 7) | (uint64_t)(D - 1 - c);
 }
 
 // Heads per workgroup: one thread group of D lanes per head, and at most half
@@ -91,7 +63,12 @@ __device__ __forceinline__ void select_block(int block, const void *q,
   constexpr int HPB = heads_per_block<D>(), NSUB = blocks_per_unit<D, G>();
   static_assert(HPB * D <= kThreads && HPB * 64 <= kThreads, "one thread group and one wave per head");
   __shared__ float qs[HPB][D];
-  __shared__ float mag[HPB][D];
+  constexpr int WPH = kThreads / 64 / HPB;      // wavefronts per head in the ranking
+  constexpr int SL = D / WPH;                   // channels each wavefront compares against
+  constexpr int CPL = D / 64;                   // channels per lane
+  static_assert(D % 64 == 0 && SL % 2 == 0, "whole wavefronts and key pairs");
+  __shared__ __attribute__((aligned(16))) uint64_t key[HPB][D];
+  __shared__ uint32_t part[HPB][WPH][D];
   const int unit = block / NSUB, h0 = (block % NSUB) * HPB;
   const int b = unit / hkv, g = unit % hkv;
   const size_t row0 = (size_t)b * hq + (size_t)g * G + h0;
@@ -127,13 +104,50 @@ __device__ __forceinline__ void select_block(int block, const void *q,
 #pragma unroll
     for (int r = 0; r < D; ++r) acc = __builtin_fmaf(qs[GRP][r], a[r], acc);
     q_prime[(row0 + GRP) * D + col] = acc;
-    mag[GRP][col] = fabsf(acc);
+    key[GRP][col] = order_key<D>(acc, col);
   };
   static_assert(HPB <= 2, "thread groups with a head");
   if (grp == 0 && nh > 0) chain(std::integral_constant<int, 0>{});
   else if constexpr (HPB > 1) { if (grp == 1 && nh > 1) chain(std::integral_constant<int, 1>{}); }
   __syncthreads();
-  if (wave < nh) select_one_head<D>(mag[wave], keep, sel_idx + (row0 + wave) * keep);
+  // Rank of channel c: the number of channels whose key is larger.  Wavefront
+  // w counts, for head w / WPH, against channels [SL * (w % WPH), + SL).
+  const int lane = j & 63;
+  {
+    const int hh = wave / WPH, p = wave % WPH;
+    if (hh < nh) {
+      uint64_t mine[CPL];
+      uint32_t r[CPL];
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) { mine[i] = key[hh][lane + 64 * i]; r[i] = 0; }
+      const uint64_t *ks = &key[hh][SL * p];
+#pragma unroll
+      for (int e = 0; e < SL; ++e)
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) r[i] += ks[e] > mine[i] ? 1u : 0u;
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) part[hh][p][lane + 64 * i] = r[i];
+    }
+  }
+  __syncthreads();
+  // Wavefront h keeps channel 0 and the channels of rank below keep - 1 of its
+  // head and writes their indices in ascending order.
+  if (wave < nh) {
+    const unsigned long long below = (1ull << lane) - 1ull;
+    int base = 0;
+    int32_t *idx = sel_idx + (row0 + wave) * keep;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int c = lane + 64 * i;
+      uint32_t rank = 0;
+#pragma unroll
+      for (int p = 0; p < WPH; ++p) rank += part[wave][p][c];
+      const bool s = c == 0 || (int)rank < keep - 1;
+      const unsigned long long m = __ballot(s);
+      if (s) idx[base + popc(m & below)] = c;
+      base += popc(m);
+    }
+  }
 }
 
 }  // namespace selb
