@@ -168,6 +168,41 @@ def test_fused_append_select_matches_separate_calls(orc, name, steps):
         assert np.array_equal(idx1.cpu().numpy(), idx2.cpu().numpy())
 
 
+@pytest.mark.parametrize("d,hq,hkv,dtype", [(64, 2, 1, "f32"), (64, 8, 2, "bf16"), (64, 16, 2, "f32"),
+                                              (128, 2, 1, "bf16"), (128, 16, 2, "f32")])
+def test_select_and_fused_step_group_shapes(orc, d, hq, hkv, dtype):
+    """Selection workgroups serve one query head (two at head_dim 64, where the
+    second thread group takes the second head): every group size at both head
+    dims, alone and in the fused append + select launch, against the oracle."""
+    wl = W.custom(f"shape_d{d}_g{hq // hkv}", 40 + d + hq, 3, hq, hkv, d, [100, 37, 64], 192,
+                  dtype=dtype)
+    say("select/fused shapes", wl.describe())
+    a, b = W.transforms(wl)
+    q = W.queries(wl)
+    for keep in sorted({1, 2, orc.keep_count(d, 40), d - 1, d}):
+        qp, idx = gpu_queries(wl, q, a, keep)
+        qpo, idxo = orc.queries(q, a, hkv, keep)
+        assert np.array_equal(qp.cpu().numpy().view(np.uint32), qpo.view(np.uint32)), keep
+        assert np.array_equal(idx.cpu().numpy(), idxo), keep
+    g1, _, _, k, v = build_gpu(wl)
+    g2, _, _, _, _ = build_gpu(wl, kv=(k, v))
+    a_d, b_d = dev_f32(a), dev_f32(b)
+    keep = orc.keep_count(d, 40)
+    x = np.random.default_rng(11).standard_normal((wl.batch, hkv, 1, d)).astype(np.float32)
+    kx = dev_input(W.round_bf16(x)[0] if dtype == "bf16" else x, dtype)
+    qd = dev_input(W.queries(wl, 1), dtype)
+    counts = dev_i32(np.ones(wl.batch, dtype=np.int32))
+    qp1, idx1 = M.append_select(g1, kx, kx, b_d, counts, qd, a_d, keep)
+    M.transform_quantize_append(g2, kx, kx, b_d, counts)
+    qp2, idx2 = M.select_channels(qd, a_d, hkv, keep)
+    torch.cuda.synchronize()
+    p1, p2 = planes_np(g1), planes_np(g2)
+    for nm in p1:
+        assert np.array_equal(p1[nm], p2[nm]), nm
+    assert np.array_equal(qp1.cpu().numpy().view(np.uint32), qp2.cpu().numpy().view(np.uint32))
+    assert np.array_equal(idx1.cpu().numpy(), idx2.cpu().numpy())
+
+
 def test_select_forced_ties(orc):
     """Duplicated, negated and signed-zero query channels: ties go to lower index."""
     d, hq = 128, 8
