@@ -827,9 +827,16 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
       kissue(S0, c_t0, 0 < nbc);
       kissue(S1, c_t0 + kBlock4, 1 < nbc);
     }
+    // A block's commit and the loads issued with it gate the barrier every
+    // wavefront of the workgroup waits on: they run at raised wave priority, so
+    // they win the issue arbitration against the logits and value work of the
+    // other workgroup on the compute unit (which otherwise, being older or not,
+    // decides who waits).
+    __builtin_amdgcn_s_setprio(1);
     kcommit(S0, sm.kb[0], c_t0);
     kissue(S0, c_t0 + 2 * kBlock4, 2 < nbc);
     block_barrier();
+    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int i = 0; i < kChunk4; ++i) {
       if (i >= nbc) break;
@@ -839,9 +846,11 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) zl[hh] = fmaxf(zl[hh], fmaxf(zs[i][hh][0], zs[i][hh][1]));
       KStage4<D> &S = (i & 1) ? S0 : S1;   // holds block i + 1
+      __builtin_amdgcn_s_setprio(1);   // commit, issue and barrier: raised, as above
       kcommit(S, sm.kb[(i + 1) & 1], p0 + kBlock4);
       kissue(S, p0 + 3 * kBlock4, i + 3 < nbc);
       block_barrier();
+      __builtin_amdgcn_s_setprio(0);
     }
     float z9[2][2];   // the extra block: committed to buffer kChunk4 & 1 by the last body
     if (nbc > kChunk4) {
@@ -906,7 +915,9 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
       VStage4<D> &V = (i % 3 == 0) ? V0 : (i % 3 == 1) ? V1 : V2;
       const int tile0 = c_t0 + kBlock4 * i + kTile4 * wave;
       if (tile0 < t_end) values(V, tile0, zs[i], mr);
+      __builtin_amdgcn_s_setprio(1);   // value loads are issued at raised priority too
       vissue(V, tile0 + 3 * kBlock4, i + 3 < nbc);
+      __builtin_amdgcn_s_setprio(0);
     }
     if (nbc > kChunk4) {   // the extra block's values are in stage kChunk4 % 3
       const int tile0 = c_t0 + kBlock4 * kChunk4 + kTile4 * wave;
