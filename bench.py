@@ -176,6 +176,25 @@ def summarize_rocprof(directory: str, kernel_regex: str, copy_mib: int) -> None:
 
 # ----------------------------------------------------------------------------- CPU baseline
 
+def cpu_model() -> str:
+    """The host CPU's model name (lscpu, else /proc/cpuinfo)."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, a, b, keep, sm, budget_s: float = 20.0):
     """The oracle, as written, on a bounded sample: one KV head (its G query heads)
     of the workload at full context: untimed cache build, then timed repeats of
@@ -223,7 +242,7 @@ def cpu_baseline(wl, a, b, keep, sm, budget_s: float = 20.0):
     # threads are busy
     used = min(threads, wl.group)
     return {"value": round(nbytes / spent / 1e9, 4), "unit": "GB/s", "cores": used,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(), "cpu_count": ncpu,
             "sample": (f"1 of {wl.hkv} KV heads ({wl.group} query heads) of the workload at "
                        f"{t_ctx} tokens: append 1 + select + decode, {reps} repeats in "
                        f"{spent:.1f}s (cache build {build_s:.1f}s untimed); OpenMP over the "
@@ -440,7 +459,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f16 MFMA operands (logit weights as two f16 limbs), f32 accumulate",
         "data": "synthetic (seeded; bf16 q/k/v, log-uniform key channel scales, channel 0 x8)",
         "config": {"workload": "ctx128k: batch 1, 32/8 heads, head_dim 128, context 131072, "
                                f"INT2 K/V groups of 32, {args.sparsity}% query-channel sparsity, "

@@ -31,7 +31,7 @@ class _Cache(C.Structure):
 
 
 _lib = None
-EXPORTS = ("dqk_status_str", "dqk_cache_plane_bytes", "dqk_transform_quantize_append",
+EXPORTS = ("dqk_status_str", "dqk_keep_count", "dqk_cache_plane_bytes", "dqk_transform_quantize_append",
            "dqk_select_channels", "dqk_append_select", "dqk_decode_workspace_bytes",
            "dqk_decode_attention",
            "dqk_dequant_reference", "dqk_bf16_decode_workspace_bytes",
@@ -50,6 +50,7 @@ def lib():
         L.dqk_status_str.restype = C.c_char_p
         L.dqk_status_str.argtypes = [C.c_int]
         for name, args in {
+            "dqk_keep_count": [I, I, P],
             "dqk_cache_plane_bytes": [I, I, I, I, P],
             "dqk_transform_quantize_append": [C.POINTER(_Cache), P, P, C.c_int, P, P, I, P],
             "dqk_select_channels": [P, C.c_int, P, I, I, I, I, I, P, P, P],
@@ -107,9 +108,11 @@ def _dtype_code(t) -> int:
 
 
 def keep_for_sparsity(head_dim: int, sparsity_pct: int) -> int:
-    """Channels kept per query head at a query-channel sparsity in percent:
-    round(head_dim * (1 - s)) with halves rounded up, in integers."""
-    return (head_dim * (100 - sparsity_pct) + 50) // 100
+    """Channels kept per query head at a query-channel sparsity in percent, as the
+    library defines it (dqk_keep_count)."""
+    out = C.c_int32(0)
+    _check(lib().dqk_keep_count(int(head_dim), int(sparsity_pct), C.byref(out)), "dqk_keep_count")
+    return int(out.value)
 
 
 def cache_plane_bytes(batch: int, hkv: int, d: int, cap: int):

@@ -5,7 +5,7 @@
 #include <math.h>
 #include <stdint.h>
 
-#include "dqk_internal.h"
+#include "dqk_host.h"
 
 namespace {
 
@@ -74,6 +74,12 @@ const char *dqk_status_str(dqk_status s) {
     case DQK_ERR_HIP: return "HIP error";
   }
   return "unknown status";
+}
+
+dqk_status dqk_keep_count(int32_t head_dim, int32_t sparsity_pct, int32_t *out_keep) {
+  if (!out_keep || head_dim < 1 || sparsity_pct < 0 || sparsity_pct > 100) return DQK_ERR_INVALID;
+  *out_keep = (int32_t)(((int64_t)head_dim * (100 - sparsity_pct) + 50) / 100);
+  return DQK_OK;
 }
 
 dqk_status dqk_cache_plane_bytes(int32_t batch, int32_t hkv, int32_t d, int32_t cap,

@@ -204,9 +204,12 @@ __device__ __forceinline__ void append_block(int block, const dqk_cache &c, cons
     if (merged && bi == 0) store_group<D, BF16>(c, b, g, g1, L, n, k_new, v_new, bcol, bmat, max_new, sm);
   }
   // Length commit: every workgroup of the row (with or without a group to store)
-  // counts itself in on the row's arrival counter after it has read the length;
-  // the last of the row's num_kv_heads * blocks_per_unit workgroups writes the
-  // new length, and the counter wraps back to zero for the next append.
+  // counts itself in on the row's arrival counter once all of its wavefronts
+  // have read the length (the barrier); the last of the row's num_kv_heads *
+  // blocks_per_unit workgroups writes the new length, and the counter wraps
+  // back to zero for the next append.  So no wavefront of the row can read the
+  // new length in this launch.
+  __syncthreads();
   if (threadIdx.x == 0) {
     const unsigned total = (unsigned)(c.num_kv_heads * blocks_per_unit);
     unsigned *arrivals = reinterpret_cast<unsigned *>(c.lengths + c.batch);

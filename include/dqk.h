@@ -13,8 +13,11 @@
  *
  * Conventions for every call:
  *  - Pointers are DEVICE pointers unless marked "host".  The caller owns all
- *    memory; the library allocates nothing, keeps no pointer after returning
- *    and holds no global state.  Calls are thread-safe.
+ *    memory; the library allocates nothing and keeps no pointer after
+ *    returning.  Its only process state is a per-device cache of the compute
+ *    unit count (queried once per device on first use by the decode, never
+ *    freed; it changes no result, only how a row's blocks are shared out over
+ *    the splits).  Calls are thread-safe.
  *  - Work is enqueued on `stream` (0 = the null stream); no call synchronizes.
  *  - Every argument the host can see is validated before anything is launched:
  *    an invalid call returns an error status and launches nothing.  A launch
@@ -77,6 +80,16 @@ typedef struct {
 
 /* Human-readable name of a status (static string). */
 const char *dqk_status_str(dqk_status s);
+
+/* Host query, no device work: channels kept per query head at a query-channel
+ * sparsity of sparsity_pct percent (tech.dede.sh summary, "Results at 128K
+ * context": 40% query-channel sparsity).  *out_keep = floor((head_dim *
+ * (100 - sparsity_pct) + 50) / 100), i.e. head_dim * (1 - s) rounded half up,
+ * in integers; channel 0 counts toward it.  77 / 51 / 128 at head_dim 128 for
+ * 40 / 60 / 0 %.  A result of 0 (sparsity 100) is not a valid keep for the
+ * selection calls.  Errors: DQK_ERR_INVALID for a null out_keep, head_dim < 1
+ * or sparsity_pct outside [0, 100]. */
+dqk_status dqk_keep_count(int32_t head_dim, int32_t sparsity_pct, int32_t *out_keep);
 
 /* Host query, no device work: byte sizes of the planes k_codes, k_scales, k_ch0,
  * k_tail, v_codes, v_scales, lengths for the given shape (out_bytes: host [7]). */

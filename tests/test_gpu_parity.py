@@ -261,6 +261,19 @@ def test_decode_ragged_edges(orc):
         assert not out[0].any()
 
 
+@pytest.mark.parametrize("hq", [32, 64])
+def test_decode_group4_empty_and_short_rows(orc, hq):
+    """Rows of 0, 1, 31, 33 and 700 tokens on the matrix-core kernel (groups of
+    four and eight, capacity a multiple of 64): an empty row gives zeros, the
+    others match the oracle, for the default split and fixed ones."""
+    wl = W.custom(f"g4-edges{hq}", 33, 5, hq, 8, 128, [0, 700, 1, 31, 33], 768, "bf16",
+                  log_uniform_key_scales=True, student_t_queries=(hq == 64))
+    g, outs, o_ref = decode_case(orc, wl, splits=(0, 64, 256, 768))
+    for out in outs:
+        assert not out[0].any()
+    decode_case(orc, wl, sparsity=0, sm_mult=0.02, splits=(0,))
+
+
 @pytest.mark.parametrize("hq,hkv,d,cap", [(1, 1, 64, 1344), (2, 1, 64, 1344), (8, 1, 64, 1344),
                                           (4, 2, 128, 1344), (16, 2, 128, 1344),
                                           (64, 8, 128, 1344), (4, 1, 64, 1344), (8, 2, 64, 1376),
@@ -339,10 +352,10 @@ def test_decode_workspace_reuse(orc):
     assert np.array_equal(fresh.view(np.uint32), out.cpu().numpy().view(np.uint32))
 
 
-@pytest.mark.parametrize("ctx", [131072, 80000])
-def test_decode_ctx128k_sampled(orc, ctx):
+@pytest.mark.parametrize("ctx,sparsity", [(131072, 40), (80000, 40), (131072, 0), (131072, 60)])
+def test_decode_ctx128k_sampled(orc, ctx, sparsity):
     """The benchmark's workload at full size (batch 1, 32/8 heads, head_dim 128,
-    131072 tokens, 40% sparsity) in its launch configuration (the default
+    131072 tokens, 40% sparsity, and the sweep's 0% and 60%) in its launch configuration (the default
     split: 512 workgroups, two per compute unit, the first-dispatched ones taking
     9/8 of the average share), at exactly 128K tokens, one past (one more block)
     and 33 past (a full key group and a tail token in the last block); and the
@@ -371,7 +384,7 @@ def test_decode_ctx128k_sampled(orc, ctx):
     cache = M.Cache(1, wl.hkv, wl.d, wl.cap)
     bm = dev_f32(b)
     ocs = {g: orc.Cache(1, 1, wl.d, wl.cap) for g in sampled}
-    keep = orc.keep_count(wl.d, 40)
+    keep = orc.keep_count(wl.d, sparsity)
     q = W.queries(wl)
     qp, idx = gpu_queries(wl, q, a, keep)
     idx_np = idx.cpu().numpy()
@@ -390,8 +403,107 @@ def test_decode_ctx128k_sampled(orc, ctx):
             qpo, idxo = orc.queries(q[:, hs], a[g:g + 1], 1, keep)
             assert np.array_equal(idx_np[:, hs], idxo), g
             err = rel_err(out[:, hs], ocs[g].decode(qpo, idxo, sm))
-            say(f"  length {ctx + extra}, KV head {g}: max rel err {err:.3e}")
+            say(f"  length {ctx + extra}, s {sparsity}%, KV head {g}: max rel err {err:.3e}")
             assert err <= REL_TOL, (extra, g, err)
+
+
+def test_decode_gqa8k_full_sampled(orc):
+    """The GQA 32/8 workload at full size (batch 4, head_dim 128, 8192 tokens,
+    40% sparsity, bf16) in its launch configuration (the default split): the
+    whole cache is built from the workload's own keys and values, and three
+    (row, KV head) units are checked against the oracle, which decodes each from
+    a one-KV-head cache of that unit (the units are independent)."""
+    wl = W.workload("gqa8k")
+    sm = W.default_sm_scale(wl.d)
+    g, a, b, k, v = build_gpu(wl)
+    keep = orc.keep_count(wl.d, 40)
+    q = W.queries(wl)
+    qp, idx = gpu_queries(wl, q, a, keep)
+    idx_np = idx.cpu().numpy()
+    out = M.decode_attention(g, qp, idx, sm).cpu().numpy()
+    for bb, gg in ((0, 0), (3, 7), (2, 4)):
+        say(f"gqa8k full: oracle for row {bb}, KV head {gg}")
+        oc = orc.Cache(1, 1, wl.d, wl.cap)
+        n = int(wl.ctx[bb])
+        oc.append(k[bb:bb + 1, gg:gg + 1, :n], v[bb:bb + 1, gg:gg + 1, :n], b[gg:gg + 1], [n])
+        hs = slice(wl.group * gg, wl.group * (gg + 1))
+        qpo, idxo = orc.queries(q[bb:bb + 1, hs], a[gg:gg + 1], 1, keep)
+        assert np.array_equal(idx_np[bb:bb + 1, hs], idxo)
+        err = rel_err(out[bb:bb + 1, hs], oc.decode(qpo, idxo, sm))
+        say(f"  max rel err {err:.3e}")
+        assert err <= REL_TOL, (bb, gg, err)
+
+
+def test_append32k_fused_steps_sampled(orc):
+    """The 32K append loop at full size (batch 8, 32/8 heads, head_dim 128, 32768
+    prefilled tokens, then 64 steps of the fused append-one-token + select launch
+    followed by the decode, 40% sparsity) as the benchmark runs it.  Two (row, KV
+    head) units hold the workload's own keys and values, prefill and appended
+    tokens; the others hold draws of the same channel scales.  After steps 0, 31
+    (the step that closes a 32-token key group) and 63 the sampled units' outputs
+    and kept sets are checked against the oracle, which replays the same appends
+    on a one-KV-head cache per unit, and their cache planes must be byte-equal."""
+    wl = W.workload("append32k")
+    ctx, sm = int(wl.ctx[0]), W.default_sm_scale(wl.d)
+    a, b = W.transforms(wl)
+    kscale = W.key_scales(wl)
+    units = [(0, 0), (5, 3)]
+    say("append32k: drawing the sampled units' tokens")
+    kv = {u: W.unit_kv(wl, u[0], u[1], 0, ctx + wl.steps, kscale) for u in units}
+    cache = M.Cache(wl.batch, wl.hkv, wl.d, wl.cap)
+    bm, ks_d = dev_f32(b), dev_f32(kscale)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(13)
+    chunk = 8192
+    for pos in range(0, ctx, chunk):
+        k = torch.randn((wl.batch, wl.hkv, chunk, wl.d), generator=gen, device="cuda")
+        k = (k * ks_d[None, :, None, :]).to(torch.bfloat16)
+        v = torch.randn((wl.batch, wl.hkv, chunk, wl.d), generator=gen, device="cuda").to(torch.bfloat16)
+        for (bb, gg), (kk, vv) in kv.items():
+            k[bb, gg] = torch.from_numpy(kk[pos:pos + chunk]).cuda().to(torch.bfloat16)
+            v[bb, gg] = torch.from_numpy(vv[pos:pos + chunk]).cuda().to(torch.bfloat16)
+        M.transform_quantize_append(cache, k, v, bm, dev_i32(np.full(wl.batch, chunk)))
+    ocs = {}
+    for (bb, gg), (kk, vv) in kv.items():
+        say(f"  oracle prefill: row {bb}, KV head {gg}")
+        oc = orc.Cache(1, 1, wl.d, wl.cap)
+        oc.append(kk[None, None, :ctx], vv[None, None, :ctx], b[gg:gg + 1], [ctx])
+        ocs[(bb, gg)] = oc
+    keep = orc.keep_count(wl.d, 40)
+    a_d = dev_f32(a)
+    ones = dev_i32(np.ones(wl.batch))
+    qp = torch.empty((wl.batch, wl.hq, wl.d), dtype=torch.float32, device="cuda")
+    idx = torch.empty((wl.batch, wl.hq, keep), dtype=torch.int32, device="cuda")
+    out = torch.empty((wl.batch, wl.hq, wl.d), dtype=torch.float32, device="cuda")
+    ws = torch.empty(M.decode_workspace_bytes(cache, wl.hq), dtype=torch.uint8, device="cuda")
+    for step in range(wl.steps):
+        x = torch.randn((2, wl.batch, wl.hkv, 1, wl.d), generator=gen, device="cuda")
+        x[0] *= ks_d[None, :, None, :]
+        for (bb, gg), (kk, vv) in kv.items():
+            x[0, bb, gg, 0] = torch.from_numpy(kk[ctx + step]).cuda()
+            x[1, bb, gg, 0] = torch.from_numpy(vv[ctx + step]).cuda()
+        x = x.to(torch.bfloat16)
+        q = W.queries(wl, step)
+        M.append_select(cache, x[0].contiguous(), x[1].contiguous(), bm, ones,
+                        dev_input(q, wl.dtype), a_d, keep, qp, idx)
+        M.decode_attention(cache, qp, idx, sm, 0, out, ws)
+        for (bb, gg), (kk, vv) in kv.items():
+            ocs[(bb, gg)].append(kk[None, None, ctx + step:ctx + step + 1],
+                                 vv[None, None, ctx + step:ctx + step + 1], b[gg:gg + 1], [1])
+        if step not in (0, 31, 63):
+            continue
+        o = out.cpu().numpy()
+        idx_np = idx.cpu().numpy()
+        planes = planes_np(cache)
+        for (bb, gg), oc in ocs.items():
+            assert int(planes["lengths"][bb]) == ctx + step + 1
+            assert_same_cache(planes, oc, unit_map=[((bb, gg), (0, 0))])
+            hs = slice(wl.group * gg, wl.group * (gg + 1))
+            qpo, idxo = orc.queries(q[bb:bb + 1, hs], a[gg:gg + 1], 1, keep)
+            assert np.array_equal(idx_np[bb:bb + 1, hs], idxo), (step, bb, gg)
+            err = rel_err(o[bb:bb + 1, hs], oc.decode(qpo, idxo, sm))
+            say(f"  step {step}, row {bb}, KV head {gg}: max rel err {err:.3e}")
+            assert err <= REL_TOL, (step, bb, gg, err)
 
 
 def test_decode_ragged64k_sampled(orc):

@@ -203,6 +203,94 @@ def test_transform_pair_keeps_dot_products(orc):
     assert err < 1e-4
 
 
+def _round_f32(x):
+    """Round an exact rational to the nearest fp32 number, ties to even (IEEE
+    binary32: 24-bit significand, exponent >= -126, subnormal quantum 2^-149)."""
+    from fractions import Fraction
+    if x == 0:
+        return np.float32(0.0)
+    sign = -1 if x < 0 else 1
+    a = abs(Fraction(x))
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    quantum = Fraction(2) ** (max(e, -126) - 23)
+    m = a / quantum
+    fl = m.numerator // m.denominator
+    rem = m - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return np.float32(sign * float(fl * quantum))
+
+
+def _fma_chain_exact(x, col, order):
+    """acc = +0; acc = fp32(x_i * m_i + acc) for i in `order`: each fused
+    multiply-add evaluated exactly in rationals and rounded once to fp32."""
+    from fractions import Fraction
+    acc = np.float32(0.0)
+    for i in order:
+        acc = _round_f32(Fraction(float(x[i])) * Fraction(float(col[i])) + Fraction(float(acc)))
+    return acc
+
+
+def test_transform_ascending_fma_chain_order(orc):
+    """The transform's reading fixes the order of the chain: ascending input
+    index, one rounding per fused multiply-add.  A crafted column where the two
+    orders round differently, then random columns of wide dynamic range, against
+    an exact-rational evaluation of each fused multiply-add; the descending
+    chain must differ somewhere, so the pin separates the two orders."""
+    # 1 + 2^-24 + 2^-24: ascending rounds each addition back to 1 (tie to even);
+    # descending sums the two small terms first, then 1 + 2^-23 is exact
+    d = 64
+    x = np.zeros(d, dtype=np.float32)
+    x[:3] = [1.0, 2.0 ** -24, 2.0 ** -24]
+    m = np.zeros((d, d), dtype=np.float32)
+    m[:3, 0] = 1.0
+    y = orc.transform(x, m)
+    assert y[0] == np.float32(1.0)
+    assert _fma_chain_exact(x, m[:, 0], range(d - 1, -1, -1)) == np.float32(1.0 + 2.0 ** -23)
+    rng = np.random.default_rng(31)
+    differs = 0
+    for d in (64, 128):
+        x = (rng.standard_normal(d) * 2.0 ** rng.integers(-12, 13, d)).astype(np.float32)
+        m = (rng.standard_normal((d, d)) * 2.0 ** rng.integers(-12, 13, (d, d))).astype(np.float32)
+        y = orc.transform(x, m)
+        for j in range(0, d, 3):
+            asc = _fma_chain_exact(x, m[:, j], range(d))
+            assert y[j].view(np.uint32) == asc.view(np.uint32), (d, j)
+            differs += asc != _fma_chain_exact(x, m[:, j], range(d - 1, -1, -1))
+    assert differs > 0
+
+
+def test_queries_use_the_kv_head_of_each_group(orc):
+    """Query head h uses A of KV head h div G.  Each KV head gets its own signed
+    power-of-two permutation matrix, so q' = q A_g is exact in fp32 and equals
+    numpy's fp64 product bit for bit; any other head-to-transform mapping
+    (h mod hkv, say) picks another permutation and fails.  The kept sets follow
+    from the exact q' by lexsort."""
+    rng = np.random.default_rng(32)
+    d, hkv, batch, keep = 64, 3, 2, 38
+    mats = []
+    for g in range(hkv):
+        m = np.zeros((d, d), dtype=np.float32)
+        m[np.arange(d), rng.permutation(d)] = rng.choice([-1.0, 1.0], d) * 2.0 ** rng.integers(-4, 5, d)
+        mats.append(m)
+    a = np.stack(mats)
+    for grp in (1, 2, 4, 8):
+        hq = hkv * grp
+        q = rng.standard_normal((batch, hq, d)).astype(np.float32)
+        qp, idx = orc.queries(q, a, hkv, keep)
+        for bb in range(batch):
+            for h in range(hq):
+                want = (q[bb, h].astype(np.float64) @ a[h // grp].astype(np.float64)).astype(np.float32)
+                assert np.array_equal(qp[bb, h].view(np.uint32), want.view(np.uint32)), (grp, bb, h)
+                c = np.arange(1, d)
+                order = np.lexsort((c, -np.abs(want[1:])))
+                assert np.array_equal(idx[bb, h], np.sort(np.concatenate([[0], c[order][:keep - 1]])))
+
+
 # ----------------------------------------------------------------------------- selection
 
 def test_keep_count_values(orc):
