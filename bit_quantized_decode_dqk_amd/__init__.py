@@ -33,7 +33,7 @@ class _Cache(C.Structure):
 _lib = None
 EXPORTS = ("dqk_status_str", "dqk_keep_count", "dqk_cache_plane_bytes", "dqk_transform_quantize_append",
            "dqk_select_channels", "dqk_append_select", "dqk_decode_workspace_bytes",
-           "dqk_decode_attention",
+           "dqk_decode_attention", "dqk_select_channels_shared", "dqk_decode_attention_shared",
            "dqk_dequant_reference", "dqk_bf16_decode_workspace_bytes",
            "dqk_bf16_decode_attention", "dqk_debug_f16_from_f32", "dqk_stream_read")
 
@@ -57,6 +57,9 @@ def lib():
             "dqk_append_select": [C.POINTER(_Cache), P, P, P, P, I, P, P, I, I, C.c_int, P, P, P],
             "dqk_decode_workspace_bytes": [C.POINTER(_Cache), I, I, P],
             "dqk_decode_attention": [C.POINTER(_Cache), P, P, I, I, C.c_float, I, P, P, S, P],
+            "dqk_select_channels_shared": [P, C.c_int, P, I, I, I, I, I, P, P, P],
+            "dqk_decode_attention_shared": [C.POINTER(_Cache), P, P, I, I, C.c_float, I, P, P, S,
+                                            P],
             "dqk_dequant_reference": [C.POINTER(_Cache), P, P, P],
             "dqk_bf16_decode_workspace_bytes": [I, I, I, I, I, I, P],
             "dqk_bf16_decode_attention": [P, P, P, P, I, I, I, I, I, C.c_float, I, P, P, S, P],
@@ -235,6 +238,45 @@ def decode_attention(cache: Cache, q_prime, sel_idx, sm_scale: float, split_toke
                                       workspace.numel() * workspace.element_size(),
                                       _stream(stream)),
            "dqk_decode_attention")
+    return out
+
+
+def select_channels_shared(q, amat, hkv: int, keep: int, q_prime=None, sel_idx=None,
+                           stream=None):
+    """Group-shared selection (dqk_select_channels_shared): q [batch][hq][d] (fp32 or
+    bf16), amat [hkv][d][d] fp32 -> (q' [batch][hq][d] fp32, idx [batch][hkv][keep])."""
+    torch = _torch()
+    batch, hq, d = q.shape
+    if q_prime is None:
+        q_prime = torch.empty((batch, hq, d), dtype=torch.float32, device=q.device)
+    if sel_idx is None:
+        sel_idx = torch.empty((batch, hkv, keep), dtype=torch.int32, device=q.device)
+    _check(lib().dqk_select_channels_shared(_ptr(q), _dtype_code(q), _ptr(amat), batch, hq, hkv,
+                                            d, keep, _ptr(q_prime), _ptr(sel_idx),
+                                            _stream(stream)),
+           "dqk_select_channels_shared")
+    return q_prime, sel_idx
+
+
+def decode_attention_shared(cache: Cache, q_prime, sel_idx, sm_scale: float,
+                            split_tokens: int = 0, out=None, workspace=None, stream=None):
+    """Decode with group-shared kept sets (dqk_decode_attention_shared): q_prime
+    [batch][hq][d] fp32, sel_idx [batch][hkv][keep] int32; returns out [batch][hq][d]."""
+    torch = _torch()
+    batch, hq, d = q_prime.shape
+    keep = int(sel_idx.shape[-1])
+    if out is None:
+        out = torch.empty((batch, hq, d), dtype=torch.float32, device=q_prime.device)
+    if workspace is None:
+        nb = decode_workspace_bytes(cache, hq, split_tokens)
+        workspace = torch.empty(max(nb, 16), dtype=torch.uint8, device=q_prime.device)
+    s = cache.struct()
+    _check(lib().dqk_decode_attention_shared(C.byref(s), _ptr(q_prime), _ptr(sel_idx), hq, keep,
+                                             float(sm_scale), split_tokens, _ptr(out),
+                                             _ptr(workspace),
+                                             workspace.numel() * workspace.element_size(),
+                                             _stream(stream)),
+           "dqk_decode_attention_shared")
     return out
 
 

@@ -160,10 +160,15 @@ dqk_status dqk_decode_workspace_bytes(const dqk_cache *cache, int32_t hq, int32_
   return DQK_OK;
 }
 
-dqk_status dqk_decode_attention(const dqk_cache *cache, const float *q_prime,
-                                const int32_t *sel_idx, int32_t hq, int32_t keep, float sm_scale,
-                                int32_t split, float *out, void *workspace, size_t ws_bytes,
-                                dqk_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and launch shared by the decode entry points (per-head or
+// group-shared kept sets).
+dqk_status decode_call(const dqk_cache *cache, const float *q_prime, const int32_t *sel_idx,
+                       bool shared, int32_t hq, int32_t keep, float sm_scale, int32_t split,
+                       float *out, void *workspace, size_t ws_bytes, dqk_stream_t stream) {
   dqk_status st = check_cache(cache);
   if (st != DQK_OK) return st;
   if (!q_prime || !sel_idx || !out) return DQK_ERR_INVALID;
@@ -179,9 +184,44 @@ dqk_status dqk_decode_attention(const dqk_cache *cache, const float *q_prime,
   const size_t need = ws_bytes_for(cache->batch, cache->num_kv_heads, hq, cache->head_dim,
                                    cache->capacity, sp);
   if (!workspace || ws_bytes < need || !aligned16(workspace)) return DQK_ERR_WORKSPACE;
-  return from_hip(dqk::launch_decode(*cache, q_prime, sel_idx, hq, keep, sm_scale, sp, even, out,
-                                     static_cast<float *>(workspace),
+  return from_hip(dqk::launch_decode(*cache, q_prime, sel_idx, shared, hq, keep, sm_scale, sp,
+                                     even, out, static_cast<float *>(workspace),
                                      reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+dqk_status dqk_decode_attention(const dqk_cache *cache, const float *q_prime,
+                                const int32_t *sel_idx, int32_t hq, int32_t keep, float sm_scale,
+                                int32_t split, float *out, void *workspace, size_t ws_bytes,
+                                dqk_stream_t stream) {
+  return decode_call(cache, q_prime, sel_idx, false, hq, keep, sm_scale, split, out, workspace,
+                     ws_bytes, stream);
+}
+
+dqk_status dqk_select_channels_shared(const void *q, dqk_dtype dtype, const float *amat,
+                                      int32_t batch, int32_t hq, int32_t hkv, int32_t d,
+                                      int32_t keep, float *q_prime, int32_t *sel_idx,
+                                      dqk_stream_t stream) {
+  if (!q || !amat || !q_prime || !sel_idx) return DQK_ERR_INVALID;
+  if (dtype != DQK_F32 && dtype != DQK_BF16) return DQK_ERR_INVALID;
+  if (batch <= 0 || hq <= 0 || hkv <= 0 || hq % hkv != 0) return DQK_ERR_INVALID;
+  if (!supported_dim(d) || !supported_group(hq, hkv)) return DQK_ERR_UNSUPPORTED;
+  if (keep < 1 || keep > d) return DQK_ERR_INVALID;
+  if ((int64_t)batch * hq > (1 << 30)) return DQK_ERR_INVALID;
+  return from_hip(dqk::launch_select_shared(q, dtype == DQK_BF16, amat, batch, hq, hkv, d, keep,
+                                            q_prime, sel_idx,
+                                            reinterpret_cast<hipStream_t>(stream)));
+}
+
+dqk_status dqk_decode_attention_shared(const dqk_cache *cache, const float *q_prime,
+                                       const int32_t *sel_idx, int32_t hq, int32_t keep,
+                                       float sm_scale, int32_t split, float *out,
+                                       void *workspace, size_t ws_bytes, dqk_stream_t stream) {
+  return decode_call(cache, q_prime, sel_idx, true, hq, keep, sm_scale, split, out, workspace,
+                     ws_bytes, stream);
 }
 
 dqk_status dqk_dequant_reference(const dqk_cache *cache, float *k_out, float *v_out,

@@ -99,7 +99,7 @@ template <int D, int G>
 __global__ __launch_bounds__(kThreads, 2) void decode_kernel(dqk_cache c,
                                                              const float *__restrict__ qp,
                                                              const int32_t *__restrict__ sel,
-                                                             int hq, int keep, float scale2,
+                                                             int shared, int hq, int keep, float scale2,
                                                              int split, int nsplit,
                                                              float *__restrict__ ws) {
   using K = Cfg<D, G>;
@@ -139,7 +139,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(dqk_cache c,
   const size_t row0 = (size_t)b * hq + (size_t)g * G;
   for (int e = tid; e < G * keep; e += kThreads) {
     const int h = e / keep;
-    const int ch = sel[(row0 + h) * keep + e % keep];
+    // the head's kept set: its own row, or its KV head's shared one
+    const int ch = sel[(shared ? (size_t)unit : row0 + h) * keep + e % keep];
     if (ch >= 0 && ch < D) {
       atomicOr(&sm.hmask[ch], 1 << h);
       sm.coefc[h][ch] = qp[(row0 + h) * D + ch] * scale2;
@@ -565,32 +566,32 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(dqk_cache c,
 }
 
 template <int D, int G>
-hipError_t launch_decode_t(const dqk_cache &c, const float *qp, const int32_t *sel, int hq,
+hipError_t launch_decode_t(const dqk_cache &c, const float *qp, const int32_t *sel, int shared, int hq,
                            int keep, float scale2, int split, float *out, float *ws,
                            hipStream_t s) {
   const int nsplit = num_splits(c.capacity, split);
   const int items = c.batch * c.num_kv_heads * nsplit;
   hipLaunchKernelGGL((decode_kernel<D, G>), dim3((unsigned)items), dim3(kThreads), 0, s, c, qp,
-                     sel, hq, keep, scale2, split, nsplit, ws);
+                     sel, shared, hq, keep, scale2, split, nsplit, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_combine(ws, c.batch, hq, c.num_kv_heads, D, nsplit, out, s);
 }
 
 template <int D>
-hipError_t launch_decode_d(const dqk_cache &c, const float *qp, const int32_t *sel, int hq,
+hipError_t launch_decode_d(const dqk_cache &c, const float *qp, const int32_t *sel, int shared, int hq,
                            int keep, float scale2, int split, bool even, float *out, float *ws,
                            hipStream_t s) {
   switch (hq / c.num_kv_heads) {
-    case 1: return launch_decode_t<D, 1>(c, qp, sel, hq, keep, scale2, split, out, ws, s);
-    case 2: return launch_decode_t<D, 2>(c, qp, sel, hq, keep, scale2, split, out, ws, s);
+    case 1: return launch_decode_t<D, 1>(c, qp, sel, shared, hq, keep, scale2, split, out, ws, s);
+    case 2: return launch_decode_t<D, 2>(c, qp, sel, shared, hq, keep, scale2, split, out, ws, s);
     case 4:
     case 8: {
       if (!decode4_supported(c, hq))
         return hq == 4 * c.num_kv_heads
-                   ? launch_decode_t<D, 4>(c, qp, sel, hq, keep, scale2, split, out, ws, s)
-                   : launch_decode_t<D, 8>(c, qp, sel, hq, keep, scale2, split, out, ws, s);
-      const hipError_t e = launch_decode4(c, qp, sel, hq, keep, scale2, split, even, ws, s);
+                   ? launch_decode_t<D, 4>(c, qp, sel, shared, hq, keep, scale2, split, out, ws, s)
+                   : launch_decode_t<D, 8>(c, qp, sel, shared, hq, keep, scale2, split, out, ws, s);
+      const hipError_t e = launch_decode4(c, qp, sel, shared != 0, hq, keep, scale2, split, even, ws, s);
       if (e != hipSuccess) return e;
       return launch_combine(ws, c.batch, hq, c.num_kv_heads, D, num_splits(c.capacity, split), out, s);
     }
@@ -600,13 +601,13 @@ hipError_t launch_decode_d(const dqk_cache &c, const float *qp, const int32_t *s
 
 }  // namespace
 
-hipError_t launch_decode(const dqk_cache &c, const float *q_prime, const int32_t *sel_idx, int hq,
-                         int keep, float sm_scale, int split, bool even, float *out, float *ws,
-                         hipStream_t s) {
+hipError_t launch_decode(const dqk_cache &c, const float *q_prime, const int32_t *sel_idx,
+                         bool shared, int hq, int keep, float sm_scale, int split, bool even,
+                         float *out, float *ws, hipStream_t s) {
   const float scale2 = sm_scale * 1.4426950408889634f;  // logits in log2 units
   if (c.head_dim == 64)
-    return launch_decode_d<64>(c, q_prime, sel_idx, hq, keep, scale2, split, even, out, ws, s);
-  return launch_decode_d<128>(c, q_prime, sel_idx, hq, keep, scale2, split, even, out, ws, s);
+    return launch_decode_d<64>(c, q_prime, sel_idx, shared ? 1 : 0, hq, keep, scale2, split, even, out, ws, s);
+  return launch_decode_d<128>(c, q_prime, sel_idx, shared ? 1 : 0, hq, keep, scale2, split, even, out, ws, s);
 }
 
 }  // namespace dqk

@@ -252,7 +252,7 @@ template <int D>
 __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
                                                                const float *__restrict__ qp,
                                                                const int32_t *__restrict__ sel,
-                                                               int hq, int keep, float scale2,
+                                                               int shared, int hq, int keep, float scale2,
                                                                int nsplit, int bps, int ncu,
                                                                float *__restrict__ ws) {
   using L = Lay4<D>;
@@ -285,7 +285,8 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
   for (int k = 0; k < SJ; ++k) {
     const int e = tid + kThreads4 * k;
     qv[k] = qp[row0 * D + e];
-    sv[k] = e < G * keep ? sel[row0 * keep + e] : -1;
+    // the head's kept set: its own row, or its KV head's shared one
+    sv[k] = e < G * keep ? (shared ? sel[(size_t)unit * keep + e % keep] : sel[row0 * keep + e]) : -1;
   }
   const int len = max(0, min(c.lengths[b], c.capacity));
   const int nblk_all = (len + kBlock4 - 1) / kBlock4;
@@ -1019,8 +1020,9 @@ bool decode4_supported(const dqk_cache &c, int hq) {
   return c.capacity % 64 == 0 && hq % (c.num_kv_heads * kG4) == 0;
 }
 
-hipError_t launch_decode4(const dqk_cache &c, const float *q_prime, const int32_t *sel_idx, int hq,
-                          int keep, float scale2, int split, bool even, float *ws, hipStream_t s) {
+hipError_t launch_decode4(const dqk_cache &c, const float *q_prime, const int32_t *sel_idx,
+                          bool shared, int hq, int keep, float scale2, int split, bool even,
+                          float *ws, hipStream_t s) {
   const int nsplit = num_splits(c.capacity, split);
   // a caller's split of whole blocks covers exactly its split tokens of every row;
   // otherwise (and always for the library's own split count) each split takes an
@@ -1037,10 +1039,10 @@ hipError_t launch_decode4(const dqk_cache &c, const float *q_prime, const int32_
     if (n > 0 && items > n && items <= 2 * n) ncu = n;
   }
   if (c.head_dim == 64)
-    hipLaunchKernelGGL((decode4_kernel<64>), grid, block, 0, s, c, q_prime, sel_idx, hq, keep, scale2, nsplit,
+    hipLaunchKernelGGL((decode4_kernel<64>), grid, block, 0, s, c, q_prime, sel_idx, shared ? 1 : 0, hq, keep, scale2, nsplit,
                        bps, ncu, ws);
   else
-    hipLaunchKernelGGL((decode4_kernel<128>), grid, block, 0, s, c, q_prime, sel_idx, hq, keep, scale2, nsplit,
+    hipLaunchKernelGGL((decode4_kernel<128>), grid, block, 0, s, c, q_prime, sel_idx, shared ? 1 : 0, hq, keep, scale2, nsplit,
                        bps, ncu, ws);
   return hipGetLastError();
 }

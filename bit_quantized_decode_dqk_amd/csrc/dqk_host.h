@@ -70,6 +70,10 @@ hipError_t launch_append(const dqk_cache &c, const void *k_new, const void *v_ne
                          const float *bmat, const int32_t *n_new, int max_new, hipStream_t s);
 hipError_t launch_select(const void *q, bool bf16, const float *amat, int batch, int hq, int hkv,
                          int d, int keep, float *q_prime, int32_t *sel_idx, hipStream_t s);
+// one kept set per (batch row, KV head), scored over the group's heads; sel_idx [batch][hkv][keep]
+hipError_t launch_select_shared(const void *q, bool bf16, const float *amat, int batch, int hq,
+                                int hkv, int d, int keep, float *q_prime, int32_t *sel_idx,
+                                hipStream_t s);
 // the append and the selection of one step in one launch;
 // q, k_new and v_new share one dtype, the selection's batch and KV heads are the cache's
 hipError_t launch_append_select(const dqk_cache &c, const void *k_new, const void *v_new,
@@ -77,14 +81,16 @@ hipError_t launch_append_select(const dqk_cache &c, const void *k_new, const voi
                                 const void *q, const float *amat, int hq, int keep,
                                 float *q_prime, int32_t *sel_idx, hipStream_t s);
 // even: the split length is the library's choice (each split then takes an equal
-// share of its row's current blocks), not the caller's
-hipError_t launch_decode(const dqk_cache &c, const float *q_prime, const int32_t *sel_idx, int hq,
-                         int keep, float sm_scale, int split, bool even, float *out, float *ws,
-                         hipStream_t s);
+// share of its row's current blocks), not the caller's; shared: sel_idx holds one
+// kept set per (batch row, KV head) [batch][hkv][keep] instead of one per query head
+hipError_t launch_decode(const dqk_cache &c, const float *q_prime, const int32_t *sel_idx,
+                         bool shared, int hq, int keep, float sm_scale, int split, bool even,
+                         float *out, float *ws, hipStream_t s);
 // the matrix-core decode: groups of a multiple of four query heads, capacity a multiple of 64
 bool decode4_supported(const dqk_cache &c, int hq);
-hipError_t launch_decode4(const dqk_cache &c, const float *q_prime, const int32_t *sel_idx, int hq,
-                          int keep, float scale2, int split, bool even, float *ws, hipStream_t s);
+hipError_t launch_decode4(const dqk_cache &c, const float *q_prime, const int32_t *sel_idx,
+                          bool shared, int hq, int keep, float scale2, int split, bool even,
+                          float *ws, hipStream_t s);
 hipError_t launch_dequant(const dqk_cache &c, float *k_out, float *v_out, hipStream_t s);
 hipError_t launch_bf16_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                               const int32_t *lengths, int batch, int hq, int hkv, int d, int ld_t,

@@ -175,6 +175,35 @@ dqk_status dqk_decode_attention(const dqk_cache *cache, const float *q_prime,
                                 void *workspace, size_t workspace_bytes,
                                 dqk_stream_t stream);
 
+/* Group-shared channel selection: one kept set for all query heads of a KV head,
+ * so that under grouped-query attention the channels dropped are dropped for the
+ * whole group and leave the key reads (tech.dede.sh summary, "Throughput on
+ * SGLang": pruning removes key channels from the cache reads; the pages state
+ * the selection per query, and this group rule is the library's reading of it
+ * for grouped heads).  q' is written exactly as by dqk_select_channels.  For each
+ * (b, KV head g): score_c = |q'_{h0,c}| + |q'_{h0+1,c}| + ... over the group's
+ * query heads h0 = g*(hq/hkv).. in ascending order, added in fp32 from +0;
+ * sel_idx[b][g] receives, ascending, channel 0 plus the keep-1 channels c >= 1 of
+ * largest score, equal scores going to the lower index.
+ * q: [batch][hq][d] of `dtype`; amat: [hkv][d][d] fp32; q_prime: [batch][hq][d]
+ * fp32; sel_idx: [batch][hkv][keep] i32; 1 <= keep <= d; hq/hkv in {1, 2, 4, 8}.
+ * Errors as dqk_select_channels. */
+dqk_status dqk_select_channels_shared(const void *q, dqk_dtype dtype, const float *amat,
+                                      int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim,
+                                      int32_t keep, float *q_prime, int32_t *sel_idx,
+                                      dqk_stream_t stream);
+
+/* Decode attention with group-shared kept sets: exactly dqk_decode_attention with
+ * every query head h of KV head g using the set sel_idx[b][g] (as produced by
+ * dqk_select_channels_shared, [batch][hkv][keep]).  The key channels outside the
+ * set are not read for the group.  Same workspace (dqk_decode_workspace_bytes),
+ * splits, results and errors. */
+dqk_status dqk_decode_attention_shared(const dqk_cache *cache, const float *q_prime,
+                                       const int32_t *sel_idx, int32_t hq, int32_t keep,
+                                       float sm_scale, int32_t split_tokens, float *out,
+                                       void *workspace, size_t workspace_bytes,
+                                       dqk_stream_t stream);
+
 /* Dense dequantized cache for checking and inspection: k_out, v_out
  * [batch][hkv][capacity][d] fp32 hold k~ and v~ as defined above for t < len and
  * zero past it.  Not on the decode path. */

@@ -68,6 +68,8 @@ def _declare(L):
     L.dqko_keep_count.argtypes = [C.c_int, C.c_int]
     L.dqko_select.argtypes = [P, C.c_int, C.c_int, P]
     L.dqko_queries.argtypes = [P, P, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, P, P]
+    L.dqko_select_shared.argtypes = [P, C.c_int, C.c_int, C.c_int, P]
+    L.dqko_queries_shared.argtypes = [P, P, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, P, P]
     L.dqko_append.argtypes = [C.POINTER(_Cache), P, P, P, P, C.c_int32]
     L.dqko_dequant.argtypes = [C.POINTER(_Cache), P, P]
     L.dqko_attend_dense.argtypes = [P, P, C.c_int, P, P, C.c_int, C.c_int, C.c_ssize_t,
@@ -142,6 +144,33 @@ def queries(q, a, hkv: int, keep: int):
     idx = np.zeros((batch, hq, keep), dtype=np.int32)
     lib().dqko_queries(_p(q), _p(a), batch, hq, hkv, d, keep, _p(qp), _p(idx))
     return qp, idx
+
+
+def select_shared(qp_group, keep: int) -> np.ndarray:
+    """One kept set for a group of query heads: qp_group [grp][d]."""
+    qp_group = _f32(qp_group)
+    grp, d = qp_group.shape
+    idx = np.zeros(keep, dtype=np.int32)
+    lib().dqko_select_shared(_p(qp_group), grp, d, keep, _p(idx))
+    return idx
+
+
+def queries_shared(q, a, hkv: int, keep: int):
+    """q [batch][hq][d], a [hkv][d][d] -> (q' [batch][hq][d], idx [batch][hkv][keep])
+    with one group-shared kept set per (batch row, KV head)."""
+    q, a = _f32(q), _f32(a)
+    batch, hq, d = q.shape
+    qp = np.zeros_like(q)
+    idx = np.zeros((batch, hkv, keep), dtype=np.int32)
+    lib().dqko_queries_shared(_p(q), _p(a), batch, hq, hkv, d, keep, _p(qp), _p(idx))
+    return qp, idx
+
+
+def per_head(idx_shared, group: int) -> np.ndarray:
+    """Group-shared kept sets [batch][hkv][keep] laid out per query head
+    [batch][hkv*group][keep] (every head of a group keeps its group's set), the
+    form the oracle's decode takes."""
+    return np.ascontiguousarray(np.repeat(np.asarray(idx_shared, dtype=np.int32), group, axis=1))
 
 
 # ----------------------------------------------------------------------------- cache

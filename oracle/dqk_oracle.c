@@ -146,15 +146,13 @@ static int ascending_i32(const void *pa, const void *pb)
     return (a > b) - (a < b);
 }
 
-/* "Dynamic channel pruning" at a given query-channel sparsity: each query keeps
- * its largest-|q'| channels.  Reading: channel 0 (the protected channel) is
- * always kept and counts toward keep; the rest are ordered by |q'| descending,
- * equal magnitudes by lower index; the kept set is emitted in ascending order. */
-void dqko_select(const float *qp, int d, int keep, int32_t *idx)
+/* Channel 0 plus the keep-1 channels c >= 1 of largest score, equal scores by
+ * lower index, emitted in ascending order. */
+static void keep_top_scores(const float *score, int d, int keep, int32_t *idx)
 {
     ranked *r = (ranked *)malloc(sizeof(ranked) * (size_t)(d > 1 ? d - 1 : 1));
     for (int c = 1; c < d; ++c) {
-        r[c - 1].mag = fabsf(qp[c]);
+        r[c - 1].mag = score[c];
         r[c - 1].c = c;
     }
     qsort(r, (size_t)(d - 1), sizeof(ranked), by_magnitude_then_index);
@@ -162,6 +160,37 @@ void dqko_select(const float *qp, int d, int keep, int32_t *idx)
     for (int i = 1; i < keep; ++i) idx[i] = r[i - 1].c;
     qsort(idx, (size_t)keep, sizeof(int32_t), ascending_i32);
     free(r);
+}
+
+/* "Dynamic channel pruning" at a given query-channel sparsity: each query keeps
+ * its largest-|q'| channels.  Reading: channel 0 (the protected channel) is
+ * always kept and counts toward keep; the rest are ordered by |q'| descending,
+ * equal magnitudes by lower index; the kept set is emitted in ascending order. */
+void dqko_select(const float *qp, int d, int keep, int32_t *idx)
+{
+    float *score = (float *)malloc(sizeof(float) * (size_t)d);
+    for (int c = 0; c < d; ++c) score[c] = fabsf(qp[c]);
+    keep_top_scores(score, d, keep, idx);
+    free(score);
+}
+
+/* Group-shared selection: one kept set for all query heads of a KV head, so that
+ * under grouped-query attention the dropped key channels are dropped for the
+ * whole group and really leave the reads (tech.dede.sh summary, "Throughput on
+ * SGLang": pruning removes key channels from the cache reads).  The pages state
+ * the per-query rule only; the group's rule here is this build's reading: the
+ * score of channel c is sum over the group's heads h (ascending) of |q'_{h,c}|,
+ * added in fp32 from +0, then the same channel-0 and tie rules. */
+void dqko_select_shared(const float *qp, int grp, int d, int keep, int32_t *idx)
+{
+    float *score = (float *)malloc(sizeof(float) * (size_t)d);
+    for (int c = 0; c < d; ++c) {
+        float s = 0.0f;
+        for (int h = 0; h < grp; ++h) s = s + fabsf(qp[(size_t)h * d + c]);
+        score[c] = s;
+    }
+    keep_top_scores(score, d, keep, idx);
+    free(score);
 }
 
 void dqko_queries(const float *q, const float *a, int batch, int hq, int hkv, int d,
@@ -174,6 +203,21 @@ void dqko_queries(const float *q, const float *a, int batch, int hq, int hkv, in
             dqko_transform(q + row * d, a + (size_t)(h / grp) * d * d, d, qp + row * d);
             dqko_select(qp + row * d, d, keep, idx + row * keep);
         }
+}
+
+void dqko_queries_shared(const float *q, const float *a, int batch, int hq, int hkv, int d,
+                         int keep, float *qp, int32_t *idx)
+{
+    int grp = hq / hkv;
+    for (int b = 0; b < batch; ++b) {
+        for (int h = 0; h < hq; ++h) {
+            size_t row = (size_t)b * hq + h;
+            dqko_transform(q + row * d, a + (size_t)(h / grp) * d * d, d, qp + row * d);
+        }
+        for (int g = 0; g < hkv; ++g)
+            dqko_select_shared(qp + ((size_t)b * hq + (size_t)g * grp) * d, grp, d, keep,
+                               idx + ((size_t)b * hkv + g) * keep);
+    }
 }
 
 /* ------------------------------------------------------------- layout */

@@ -83,6 +83,17 @@ void dqko_select(const float *qp, int d, int keep, int32_t *idx);
 void dqko_queries(const float *q, const float *a, int batch, int hq, int hkv, int d,
                   int keep, float *qp, int32_t *idx);
 
+/* Group-shared selection for the grp query heads of one KV head, qp[grp][d]:
+ * score_c = |q'_{0,c}| + |q'_{1,c}| + ... in fp32 from +0 in ascending head
+ * order; channel 0 plus the keep-1 channels c >= 1 of largest score (equal
+ * scores: lower index first), ascending, to idx[keep]. */
+void dqko_select_shared(const float *qp, int grp, int d, int keep, int32_t *idx);
+
+/* q' [batch][hq][d] as dqko_queries, and one group-shared kept set per (batch
+ * row, KV head): idx [batch][hkv][keep]. */
+void dqko_queries_shared(const float *q, const float *a, int batch, int hq, int hkv, int d,
+                         int keep, float *qp, int32_t *idx);
+
 /* Append n_new[b] tokens per batch row (clamped to max_new and to the free
  * capacity).  k_new, v_new: [batch][hkv][max_new][d] fp32; bm: [hkv][d][d].
  * Writes the new tokens at positions lengths[b].., then lengths[b] += n. */

@@ -352,8 +352,10 @@ def test_decode_workspace_reuse(orc):
     assert np.array_equal(fresh.view(np.uint32), out.cpu().numpy().view(np.uint32))
 
 
-@pytest.mark.parametrize("ctx,sparsity", [(131072, 40), (80000, 40), (131072, 0), (131072, 60)])
-def test_decode_ctx128k_sampled(orc, ctx, sparsity):
+@pytest.mark.parametrize("ctx,sparsity,shared", [(131072, 40, False), (80000, 40, False),
+                                                 (131072, 0, False), (131072, 60, False),
+                                                 (131072, 40, True)])
+def test_decode_ctx128k_sampled(orc, ctx, sparsity, shared):
     """The benchmark's workload at full size (batch 1, 32/8 heads, head_dim 128,
     131072 tokens, 40% sparsity, and the sweep's 0% and 60%) in its launch configuration (the default
     split: 512 workgroups, two per compute unit, the first-dispatched ones taking
@@ -386,8 +388,15 @@ def test_decode_ctx128k_sampled(orc, ctx, sparsity):
     ocs = {g: orc.Cache(1, 1, wl.d, wl.cap) for g in sampled}
     keep = orc.keep_count(wl.d, sparsity)
     q = W.queries(wl)
-    qp, idx = gpu_queries(wl, q, a, keep)
-    idx_np = idx.cpu().numpy()
+    if shared:   # one kept set per KV head, checked, then laid out per head for the oracle
+        qp, idx = M.select_channels_shared(dev_input(q, wl.dtype), dev_f32(a), wl.hkv, keep)
+        _, idxo_all = orc.queries_shared(q, a, wl.hkv, keep)
+        assert np.array_equal(idx.cpu().numpy(), idxo_all)
+        idx_np = orc.per_head(idxo_all, wl.group)
+    else:
+        qp, idx = gpu_queries(wl, q, a, keep)
+        idx_np = idx.cpu().numpy()
+    decode = M.decode_attention_shared if shared else M.decode_attention
     pos = 0
     for extra in extras:
         n = ctx + extra - pos
@@ -397,10 +406,12 @@ def test_decode_ctx128k_sampled(orc, ctx, sparsity):
         for g, (kk, vv) in sampled.items():
             ocs[g].append(kk[None, None, pos:pos + n], vv[None, None, pos:pos + n], b[g:g + 1], [n])
         pos += n
-        out = M.decode_attention(cache, qp, idx, sm).cpu().numpy()
+        out = decode(cache, qp, idx, sm).cpu().numpy()
         for g in sampled:
             hs = slice(4 * g, 4 * g + 4)
             qpo, idxo = orc.queries(q[:, hs], a[g:g + 1], 1, keep)
+            if shared:
+                idxo = idx_np[:, hs]
             assert np.array_equal(idx_np[:, hs], idxo), g
             err = rel_err(out[:, hs], ocs[g].decode(qpo, idxo, sm))
             say(f"  length {ctx + extra}, s {sparsity}%, KV head {g}: max rel err {err:.3e}")
@@ -683,3 +694,86 @@ def test_bf16_decode_matches_plain_attention(orc, lens, sm_mult):
         err = rel_err(out, ref)
         say(f"  split {sp}: {err:.3e}")
         assert err <= REL_TOL
+
+
+# ----------------------------------------------------------------------------- group-shared selection
+
+@pytest.mark.parametrize("name", W.WORKLOADS)
+def test_select_shared_matches_oracle(orc, name):
+    """Group-shared kept sets (one per row and KV head, scored by the fp32 sum of
+    |q'| over the group's heads in ascending order) and q' bit for bit."""
+    wl = W.workload(name)
+    a, _ = W.transforms(wl)
+    q = W.queries(wl)
+    for keep in sorted({1, 2, orc.keep_count(wl.d, 60), orc.keep_count(wl.d, 40), wl.d - 1, wl.d}):
+        qp, idx = M.select_channels_shared(dev_input(q, wl.dtype), dev_f32(a), wl.hkv, keep)
+        qpo, idxo = orc.queries_shared(q, a, wl.hkv, keep)
+        assert np.array_equal(qp.cpu().numpy().view(np.uint32), qpo.view(np.uint32)), keep
+        assert np.array_equal(idx.cpu().numpy(), idxo), keep
+
+
+@pytest.mark.parametrize("d,hq,hkv,dtype", [(64, 2, 2, "f32"), (64, 8, 2, "bf16"), (64, 16, 2, "f32"),
+                                              (128, 4, 2, "bf16"), (128, 16, 2, "f32"),
+                                              (128, 8, 8, "bf16")])
+def test_select_shared_group_shapes_and_ties(orc, d, hq, hkv, dtype):
+    """Every group size at both head dims, and forced ties: duplicated, negated
+    and signed-zero query values under an identity transform."""
+    wl = W.custom(f"sh_d{d}_g{hq // hkv}", 60 + d + hq, 3, hq, hkv, d, [64, 64, 64], 64, dtype=dtype)
+    a, _ = W.transforms(wl)
+    q = W.queries(wl)
+    for keep in sorted({1, 2, orc.keep_count(d, 40), d - 1, d}):
+        qp, idx = M.select_channels_shared(dev_input(q, dtype), dev_f32(a), hkv, keep)
+        qpo, idxo = orc.queries_shared(q, a, hkv, keep)
+        assert np.array_equal(qp.cpu().numpy().view(np.uint32), qpo.view(np.uint32)), keep
+        assert np.array_equal(idx.cpu().numpy(), idxo), keep
+    rng = np.random.default_rng(61)
+    qt = rng.choice(np.array([0.0, -0.0, 1.0, -1.0, 2.5, -2.5], dtype=np.float32), (3, hq, d))
+    eye = np.stack([np.eye(d, dtype=np.float32)] * hkv)
+    for keep in (1, 20, d // 2, d):
+        qp, idx = M.select_channels_shared(dev_f32(qt), dev_f32(eye), hkv, keep)
+        qpo, idxo = orc.queries_shared(qt, eye, hkv, keep)
+        assert np.array_equal(idx.cpu().numpy(), idxo), keep
+        assert np.array_equal(qp.cpu().numpy().view(np.uint32), qpo.view(np.uint32))
+
+
+def decode_shared_case(orc, wl, sparsity=40, sm_mult=1.0, splits=(0,)):
+    say("decode shared", wl.describe(), "s", sparsity, "splits", splits)
+    g, a, b, k, v = build_gpu(wl)
+    ref = build_oracle(orc, wl, k, v, b)
+    keep = orc.keep_count(wl.d, sparsity)
+    q = W.queries(wl)
+    qp, idx = M.select_channels_shared(dev_input(q, wl.dtype), dev_f32(a), wl.hkv, keep)
+    qpo, idxo = orc.queries_shared(q, a, wl.hkv, keep)
+    assert np.array_equal(idx.cpu().numpy(), idxo)
+    sm = W.default_sm_scale(wl.d) * sm_mult
+    o_ref = ref.decode(qpo, orc.per_head(idxo, wl.group), sm)
+    outs = []
+    for sp in splits:
+        out = M.decode_attention_shared(g, qp, idx, sm, split_tokens=sp).cpu().numpy()
+        err = rel_err(out, o_ref)
+        say(f"  split {sp}: max rel err {err:.3e}")
+        assert err <= REL_TOL, (sp, err)
+        outs.append(out)
+    # the same sets laid out per head through the per-head decode: bitwise equal
+    per = torch.from_numpy(orc.per_head(idx.cpu().numpy(), wl.group)).cuda()
+    for sp, out in zip(splits, outs):
+        again = M.decode_attention(g, qp, per, sm, split_tokens=sp).cpu().numpy()
+        assert np.array_equal(again.view(np.uint32), out.view(np.uint32)), sp
+    return outs
+
+
+@pytest.mark.parametrize("hq,hkv,d,cap,lens", [(1, 1, 64, 1024, [1000]), (4, 2, 128, 1344, [700, 1333]),
+                                                (32, 8, 128, 5056, [5000, 2049, 0]),
+                                                (64, 8, 128, 4032, [4000, 31]),
+                                                (32, 8, 128, 1376, [1300, 77])])
+def test_decode_shared_matches_oracle(orc, hq, hkv, d, cap, lens):
+    """Decode with group-shared kept sets on every kernel: groups of one and two
+    (general kernel), four and eight (matrix-core kernel, capacity a multiple of
+    64) and four with a capacity that is not (general kernel); an empty row."""
+    wl = W.custom(f"sh{hq}-{hkv}-{d}", 70 + hq, len(lens), hq, hkv, d, lens, cap, "bf16",
+                  log_uniform_key_scales=True, student_t_queries=(hq == 64))
+    outs = decode_shared_case(orc, wl, splits=(0, 64, 1024))
+    if 0 in lens:
+        for out in outs:
+            assert not out[lens.index(0)].any()
+    decode_shared_case(orc, wl, sparsity=60, sm_mult=0.05)

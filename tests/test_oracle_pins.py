@@ -618,3 +618,109 @@ def test_value_packing_layout(orc):
                 want |= int(u[t, ch]) << (2 * (t % 16))
             assert int(c.v_codes[0, 0, blk, ch]) == want
     assert np.all(c.v_scales[0, 0, :n] == 0x3C00)
+
+
+# ----------------------------------------------------------------------------- group-shared selection
+
+def _score_beats(score, a, b):
+    return score[a] > score[b] or (score[a] == score[b] and a < b)
+
+
+def test_select_shared_single_head_is_per_head(orc):
+    """A group of one: the score is |q'| (0 + |x| is exact), so the shared set is
+    the per-head set, itself pinned by brute force and lexsort."""
+    rng = np.random.default_rng(40)
+    for d in (8, 64, 128):
+        for keep in (1, 2, d // 2, d - 1, d):
+            qp = rng.standard_normal((1, d)).astype(np.float32)
+            assert np.array_equal(orc.select_shared(qp, keep), orc.select(qp[0], keep))
+
+
+def test_select_shared_equal_magnitudes_match_one_head(orc):
+    """Heads whose |q'| rows are equal (signs flipped at random) and hold at most
+    20 significant bits: every partial sum is exact, so score = G |q'| and the
+    shared set is that of any one head."""
+    rng = np.random.default_rng(41)
+    for grp in (2, 4, 8):
+        for d in (64, 128):
+            row = (rng.integers(-(1 << 12), 1 << 12, d) / 256.0).astype(np.float32)
+            qp = (row[None] * rng.choice([-1.0, 1.0], (grp, d))).astype(np.float32)
+            for keep in (1, 38, 51, 77, d):
+                if keep <= d:
+                    assert np.array_equal(orc.select_shared(qp, keep), orc.select(row, keep))
+
+
+def test_select_shared_brute_force_tiny(orc):
+    """Every kept set containing channel 0 is enumerated; exactly one has every
+    kept channel >= 1 beating every dropped one on (score desc, index asc), where
+    the score is the fp32 sum of |q'| over the group's heads in ascending order
+    (numpy float32 scalars: one IEEE rounding per addition)."""
+    rng = np.random.default_rng(42)
+    for trial in range(200):
+        d = int(rng.integers(2, 11))
+        grp = int(rng.choice([1, 2, 3, 4, 8]))
+        keep = int(rng.integers(1, d + 1))
+        qp = rng.standard_normal((grp, d)).astype(np.float32)
+        if trial % 3 == 0:   # forced ties
+            qp = rng.choice(np.array([0.0, -0.0, 1.5, -1.5, 2.0], dtype=np.float32), (grp, d))
+        score = []
+        for c in range(d):
+            acc = np.float32(0.0)
+            for h in range(grp):
+                acc = np.float32(acc + np.float32(abs(qp[h, c])))
+            score.append(acc)
+        valid = []
+        for rest in itertools.combinations(range(1, d), keep - 1):
+            kept = set(rest)
+            dropped = [c for c in range(1, d) if c not in kept]
+            if all(_score_beats(score, a, b) for a in kept for b in dropped):
+                valid.append(sorted((0,) + rest))
+        assert len(valid) == 1
+        assert list(orc.select_shared(qp, keep)) == valid[0]
+
+
+def test_select_shared_summation_order(orc):
+    """The group's score is added in ascending head order.  Channel 1 holds
+    1, 2^-24, 2^-24 over three heads: ascending, each addition ties and rounds
+    to even, leaving 1; channel 2 holds 2^-24, 2^-24, 1: ascending gives 2^-23,
+    then 1 + 2^-23 (exact).  So channel 2 wins the single free slot; summed in
+    descending order the two scores would swap and channel 1 would win."""
+    qp = np.zeros((3, 4), dtype=np.float32)
+    qp[:, 1] = [1.0, 2.0 ** -24, 2.0 ** -24]
+    qp[:, 2] = [2.0 ** -24, 2.0 ** -24, 1.0]
+    assert list(orc.select_shared(qp, 2)) == [0, 2]
+    assert list(orc.select_shared(qp[::-1].copy(), 2)) == [0, 1]
+
+
+def test_select_shared_large_against_lexsort(orc):
+    rng = np.random.default_rng(43)
+    for grp in (2, 4, 8):
+        for d in (64, 128):
+            for keep in (1, 38, 51, 77, d):
+                if keep > d:
+                    continue
+                qp = rng.standard_normal((grp, d)).astype(np.float32)
+                score = np.zeros(d, dtype=np.float32)
+                for h in range(grp):
+                    score = (score + np.abs(qp[h])).astype(np.float32)
+                c = np.arange(1, d)
+                order = np.lexsort((c, -score[1:]))
+                ref = np.sort(np.concatenate([[0], c[order][:keep - 1]]))
+                assert np.array_equal(orc.select_shared(qp, keep), ref)
+
+
+def test_queries_shared_groups(orc):
+    """q' equals the per-head call's; each (row, KV head) set is the shared
+    selection of that group's rows."""
+    wl = W.workload("gqa8k", batch=2, ctx=64)
+    a, _ = W.transforms(wl)
+    q = W.queries(wl)
+    qp1, _ = orc.queries(q, a, wl.hkv, 77)
+    qp2, idx = orc.queries_shared(q, a, wl.hkv, 77)
+    assert np.array_equal(qp1.view(np.uint32), qp2.view(np.uint32))
+    assert idx.shape == (2, wl.hkv, 77)
+    for bb in range(2):
+        for g in range(wl.hkv):
+            rows = qp1[bb, g * wl.group:(g + 1) * wl.group]
+            assert np.array_equal(idx[bb, g], orc.select_shared(rows, 77))
+    assert orc.per_head(idx, wl.group).shape == (2, wl.hq, 77)
