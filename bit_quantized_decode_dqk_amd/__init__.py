@@ -34,6 +34,7 @@ _lib = None
 EXPORTS = ("dqk_status_str", "dqk_keep_count", "dqk_cache_plane_bytes", "dqk_transform_quantize_append",
            "dqk_select_channels", "dqk_append_select", "dqk_decode_workspace_bytes",
            "dqk_decode_attention", "dqk_select_channels_shared", "dqk_decode_attention_shared",
+           "dqk_decode_attention_noalloc",
            "dqk_dequant_reference", "dqk_bf16_decode_workspace_bytes",
            "dqk_bf16_decode_attention", "dqk_debug_f16_from_f32", "dqk_stream_read")
 
@@ -58,6 +59,7 @@ def lib():
             "dqk_decode_workspace_bytes": [C.POINTER(_Cache), I, I, P],
             "dqk_decode_attention": [C.POINTER(_Cache), P, P, I, I, C.c_float, I, P, P, S, P],
             "dqk_select_channels_shared": [P, C.c_int, P, I, I, I, I, I, P, P, P],
+            "dqk_decode_attention_noalloc": [C.POINTER(_Cache), P, P, I, I, C.c_float, I, P, P],
             "dqk_decode_attention_shared": [C.POINTER(_Cache), P, P, I, I, C.c_float, I, P, P, S,
                                             P],
             "dqk_dequant_reference": [C.POINTER(_Cache), P, P, P],
@@ -238,6 +240,28 @@ def decode_attention(cache: Cache, q_prime, sel_idx, sm_scale: float, split_toke
                                       workspace.numel() * workspace.element_size(),
                                       _stream(stream)),
            "dqk_decode_attention")
+    return out
+
+
+DECODE_SCRATCH_BYTES = 16 << 20
+
+
+def decode_attention_noalloc(cache: Cache, q_prime, sel_idx, sm_scale: float,
+                             split_tokens: int = 0, out=None, stream=None):
+    """dqk_decode_attention_noalloc: the per-head decode with the split partials in
+    the library's device scratch (no workspace; the library allocates nothing).
+    Pass `out` to keep the whole call free of allocation.  Calls that overlap on
+    one GPU race on the scratch."""
+    torch = _torch()
+    batch, hq, d = q_prime.shape
+    keep = int(sel_idx.shape[-1])
+    if out is None:
+        out = torch.empty((batch, hq, d), dtype=torch.float32, device=q_prime.device)
+    s = cache.struct()
+    _check(lib().dqk_decode_attention_noalloc(C.byref(s), _ptr(q_prime), _ptr(sel_idx), hq, keep,
+                                              float(sm_scale), split_tokens, _ptr(out),
+                                              _stream(stream)),
+           "dqk_decode_attention_noalloc")
     return out
 
 

@@ -34,6 +34,7 @@ SOURCES = {
     "dqk_bf16.hip": [],
     "dqk_combine.hip": [],
     "dqk_probe.hip": [],
+    "dqk_noalloc.hip": [],
 }
 
 COMMON = ["-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",

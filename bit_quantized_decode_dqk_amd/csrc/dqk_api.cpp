@@ -165,10 +165,12 @@ dqk_status dqk_decode_workspace_bytes(const dqk_cache *cache, int32_t hq, int32_
 namespace {
 
 // Validation and launch shared by the decode entry points (per-head or
-// group-shared kept sets).
+// group-shared kept sets; the caller's workspace, or with use_scratch the
+// library's device scratch, which then bounds the partials' size).
 dqk_status decode_call(const dqk_cache *cache, const float *q_prime, const int32_t *sel_idx,
                        bool shared, int32_t hq, int32_t keep, float sm_scale, int32_t split,
-                       float *out, void *workspace, size_t ws_bytes, dqk_stream_t stream) {
+                       float *out, void *workspace, size_t ws_bytes, dqk_stream_t stream,
+                       bool use_scratch = false) {
   dqk_status st = check_cache(cache);
   if (st != DQK_OK) return st;
   if (!q_prime || !sel_idx || !out) return DQK_ERR_INVALID;
@@ -183,7 +185,14 @@ dqk_status decode_call(const dqk_cache *cache, const float *q_prime, const int32
   const int sp = decode_split(cache, hq, split, &even);
   const size_t need = ws_bytes_for(cache->batch, cache->num_kv_heads, hq, cache->head_dim,
                                    cache->capacity, sp);
-  if (!workspace || ws_bytes < need || !aligned16(workspace)) return DQK_ERR_WORKSPACE;
+  if (use_scratch) {
+    if (need > dqk::kScratchBytes) return DQK_ERR_WORKSPACE;
+    float *scratch = nullptr;
+    if (dqk::decode_scratch(&scratch) != hipSuccess) return DQK_ERR_HIP;
+    workspace = scratch;
+  } else if (!workspace || ws_bytes < need || !aligned16(workspace)) {
+    return DQK_ERR_WORKSPACE;
+  }
   return from_hip(dqk::launch_decode(*cache, q_prime, sel_idx, shared, hq, keep, sm_scale, sp,
                                      even, out, static_cast<float *>(workspace),
                                      reinterpret_cast<hipStream_t>(stream)));
@@ -199,6 +208,14 @@ dqk_status dqk_decode_attention(const dqk_cache *cache, const float *q_prime,
                                 dqk_stream_t stream) {
   return decode_call(cache, q_prime, sel_idx, false, hq, keep, sm_scale, split, out, workspace,
                      ws_bytes, stream);
+}
+
+dqk_status dqk_decode_attention_noalloc(const dqk_cache *cache, const float *q_prime,
+                                        const int32_t *sel_idx, int32_t hq, int32_t keep,
+                                        float sm_scale, int32_t split, float *out,
+                                        dqk_stream_t stream) {
+  return decode_call(cache, q_prime, sel_idx, false, hq, keep, sm_scale, split, out, nullptr, 0,
+                     stream, true);
 }
 
 dqk_status dqk_select_channels_shared(const void *q, dqk_dtype dtype, const float *amat,

@@ -101,6 +101,13 @@ hipError_t launch_f16_convert(const float *x, uint16_t *out, size_t n, hipStream
 constexpr int kStreamReadSinkWords = DQK_STREAM_READ_SINK_WORDS;   // 2048 workgroups x 4 wavefronts
 hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t s);
 
+// Device scratch of the decode entry point that allocates nothing: the split
+// partials of one call, at most kScratchBytes (one file-scope device array per
+// GPU).  decode_scratch gives the array's device address on the current device
+// (looked up on the first call per device and kept).
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+hipError_t decode_scratch(float **ptr);
+
 // Workspace: per work item (unit, split) and query head of its group:
 // m, l, two pad floats (keeps o 16-byte aligned), o[d].
 constexpr int kPartialHead = 4;

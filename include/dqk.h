@@ -175,6 +175,26 @@ dqk_status dqk_decode_attention(const dqk_cache *cache, const float *q_prime,
                                 void *workspace, size_t workspace_bytes,
                                 dqk_stream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): dqk_decode_attention
+ * without a workspace argument.  Same arguments, kernels, splits, results and
+ * errors, except that the split partials go to the library's own device
+ * scratch: one file-scope array of DQK_DECODE_SCRATCH_BYTES per GPU, held from
+ * the library's load until the process ends.  Its device address is looked up
+ * once per device, on the first call with that device current.  The call
+ * allocates nothing (no hipMalloc or hipFree, no allocating library routine).
+ * Errors: DQK_ERR_WORKSPACE when the partials this shape and split need
+ * (dqk_decode_workspace_bytes) exceed DQK_DECODE_SCRATCH_BYTES; DQK_ERR_HIP if
+ * the scratch address cannot be looked up.  Every call on one GPU uses that
+ * GPU's one array: calls that overlap on a GPU (on different streams or host
+ * threads) race and must be ordered by the caller.  The array keeps the last
+ * call's contents; no call needs it cleared. */
+#define DQK_DECODE_SCRATCH_BYTES ((size_t)16 << 20)
+dqk_status dqk_decode_attention_noalloc(const dqk_cache *cache, const float *q_prime,
+                                        const int32_t *sel_idx, int32_t hq, int32_t keep,
+                                        float sm_scale, int32_t split_tokens, float *out,
+                                        dqk_stream_t stream);
+
 /* Group-shared channel selection: one kept set for all query heads of a KV head,
  * so that under grouped-query attention the channels dropped are dropped for the
  * whole group and leave the key reads (tech.dede.sh summary, "Throughput on

@@ -129,6 +129,24 @@ def test_decode_validation_without_gpu():
     assert L.dqk_decode_attention(c, q, idx, 8, 77, 0.1, 0, out, ws + 4, big, None) == WORKSPACE
 
 
+def test_noalloc_decode_validation_without_gpu():
+    """The decode entry point without a workspace validates like the decode and
+    refuses, before anything is launched, a shape whose partials exceed its
+    16 MiB device scratch."""
+    L = M.lib()
+    q, idx, out = 0x20000, 0x30000, 0x40000
+    c = C.byref(fake_cache())
+    assert L.dqk_decode_attention_noalloc(c, None, idx, 8, 77, 0.1, 0, out, None) == INVALID
+    assert L.dqk_decode_attention_noalloc(c, q, idx, 8, 0, 0.1, 0, out, None) == INVALID
+    assert L.dqk_decode_attention_noalloc(c, q, idx, 6, 77, 0.1, 0, out, None) == UNSUPPORTED
+    assert L.dqk_decode_attention_noalloc(c, q, idx, 8, 77, 0.1, 48, out, None) == INVALID
+    big = C.byref(fake_cache(batch=64, num_kv_heads=8, capacity=131072))
+    need = C.c_size_t(0)
+    assert L.dqk_decode_workspace_bytes(big, 32, 256, C.byref(need)) == OK
+    assert need.value > M.DECODE_SCRATCH_BYTES
+    assert L.dqk_decode_attention_noalloc(big, q, idx, 32, 77, 0.1, 256, out, None) == WORKSPACE
+
+
 def test_stream_read_validation_without_gpu():
     """The read probe rejects null or misaligned pointers and sizes that are not
     whole 16-byte elements before launching anything."""
