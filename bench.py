@@ -443,8 +443,8 @@ def main():
 
     extras = {}
     if not args.no_extras:
-        extras = run_extras(M, torch, wl, caches, a_d, step_q, qp, idx, out, ws, k_d, v_d, sm,
-                            args, roof_us)
+        extras = run_extras(M, torch, wl, caches, a_d, b_d, step_q, qp, idx, out, ws, k_d, v_d,
+                            sm, args, roof_us)
         extras["other_workloads"] = run_configs(M, torch)
         extras["stream_peak"] = stream_peak(M, torch)
 
@@ -485,27 +485,67 @@ def main():
         if read_peak:   # the practical ceiling: a plain streaming read measured in this process
             result["roofline"]["measured_read_peak"] = read_peak
             result["roofline"]["frac_of_measured_read_peak"] = round(roof_gbs / read_peak, 4)
+    if extras:
+        result["vs_pages"] = pages_comparison(M, wl, extras, roof_us, roof_bytes)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         result["cpu_baseline"] = cpu_baseline(wl, a, b, keep, sm)
     print(json.dumps(result), flush=True)
 
 
-def time_decode(M, torch, wl, caches, q, a_d, keep, sm, split, out, ws, n=40, skip=5):
+def pages_comparison(M, wl, extras, dec_us, dec_bytes):
+    """Our computed analogues of the three figures the pages give for Dual-QK at 128K
+    context (tech.dede.sh summary, "Results at 128K context" and "Throughput on
+    SGLang"; arXiv abstract): 6.8x KV-cache compression, an estimated 8.3x reduction
+    of KV reads, and up to 3.75x decode throughput, each against unpruned BF16.  The
+    pages' format, models and hardware are not stated, so theirs are context only."""
+    ctx = int(wl.ctx[0])
+    units = wl.batch * wl.hkv
+    bf16_kv = units * ctx * wl.d * 2 * 2
+    planes = M.cache_plane_bytes(wl.batch, wl.hkv, wl.d, ctx)[:6]   # codes, scales, ch0, tail
+    out = {"storage_ratio_vs_bf16": {"ours": round(bf16_kv / sum(planes), 3), "pages": 6.8,
+                                     "basis": "bf16 K+V bytes / stored INT2 planes at 131072 tokens"},
+           "read_reduction_vs_bf16": {"ours_per_head_selection": round(bf16_kv / dec_bytes, 3),
+                                      "pages_estimate": 8.3,
+                                      "basis": "bf16 K+V bytes / algorithmic bytes of one decode"}}
+    sh = extras.get("decode_shared_s40")
+    if sh:
+        out["read_reduction_vs_bf16"]["ours_group_shared_selection"] = round(bf16_kv / sh["bytes"], 3)
+    bf = extras.get("bf16_unpruned_decode")
+    if bf:
+        sp = {"measured": round(bf["us"] / dec_us, 3), "pages_up_to": 3.75,
+              "basis": "bf16 comparator time / pruned INT2 decode time, same context and GPU"}
+        peak = extras.get("stream_peak", {}).get("read_GB/s")
+        if peak:   # the bf16 read at the best measured read rate: a comparator at its ceiling
+            sp["vs_bf16_at_measured_read_ceiling"] = round(bf["bytes"] / peak / 1e3 / dec_us, 3)
+        out["decode_speedup_vs_bf16"] = sp
+    return out
+
+
+def time_decode(M, torch, wl, caches, q, a_d, keep, sm, split, out, ws, n=40, skip=5,
+                shared=False):
     """Back-to-back decode launches (partial + combine) over the rotating caches at
     their current lengths, each bracketed by HIP events on the launch stream; the host
     stays ahead of the GPU, so an interval is the two kernels and the gap between
-    them.  Returns (mean us per launch, mean algorithmic bytes per launch)."""
+    them.  shared: group-shared kept sets (one per KV head).  Returns (mean us per
+    launch, mean algorithmic bytes per launch)."""
     qp = torch.empty((wl.batch, wl.hq, wl.d), dtype=torch.float32, device=out.device)
-    idx = torch.empty((wl.batch, wl.hq, keep), dtype=torch.int32, device=out.device)
-    M.select_channels(q, a_d, wl.hkv, keep, qp, idx)
-    idx_np = idx.cpu().numpy()
+    if shared:
+        idx = torch.empty((wl.batch, wl.hkv, keep), dtype=torch.int32, device=out.device)
+        M.select_channels_shared(q, a_d, wl.hkv, keep, qp, idx)
+        idx_np = np.repeat(idx.cpu().numpy(), wl.group, axis=1)   # the same set for each head
+        decode = M.decode_attention_shared
+    else:
+        idx = torch.empty((wl.batch, wl.hq, keep), dtype=torch.int32, device=out.device)
+        M.select_channels(q, a_d, wl.hkv, keep, qp, idx)
+        idx_np = idx.cpu().numpy()
+        decode = M.decode_attention
     nbytes = [decode_bytes(idx_np, c.lengths.cpu().numpy(), wl.hkv, wl.d, keep) for c in caches]
     ts = []
     for i in range(n):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        M.decode_attention(caches[i % len(caches)], qp, idx, sm, split, out, ws)
+        decode(caches[i % len(caches)], qp, idx, sm, split, out, ws)
         e1.record()
         ts.append((e0, e1))
     torch.cuda.synchronize()
@@ -513,7 +553,7 @@ def time_decode(M, torch, wl, caches, q, a_d, keep, sm, split, out, ws, n=40, sk
     return us, float(np.mean([nbytes[i % len(caches)] for i in range(skip, n)]))
 
 
-def run_extras(M, torch, wl, caches, a_d, step_q, qp, idx, out, ws, k_d, v_d, sm, args,
+def run_extras(M, torch, wl, caches, a_d, b_d, step_q, qp, idx, out, ws, k_d, v_d, sm, args,
                dec_us):
     """Decode-only timings for the sparsity sweep and the unpruned BF16 comparator."""
     res = {}
@@ -522,8 +562,54 @@ def run_extras(M, torch, wl, caches, a_d, step_q, qp, idx, out, ws, k_d, v_d, sm
         us, nb = time_decode(M, torch, wl, caches, step_q[0], a_d, keep, sm, args.split, out, ws)
         res[f"decode_s{s}"] = {"us": round(us, 2), "GB/s": round(nb / us / 1e3, 1),
                                "bytes": int(nb)}
-    # unpruned bf16 decode over the raw cache (2 copies rotate: 537 MB each)
+    # group-shared selection: one kept set per KV head, so the dropped channels leave
+    # the key reads of the whole group
+    keep = M.keep_for_sparsity(wl.d, 40)
+    us, nb = time_decode(M, torch, wl, caches, step_q[0], a_d, keep, sm, args.split, out, ws,
+                         shared=True)
+    res["decode_shared_s40"] = {"us": round(us, 2), "GB/s": round(nb / us / 1e3, 1),
+                                "bytes": int(nb), "frac_of_8TB/s": round(nb / us / 1e3 / HBM_PEAK_GBS, 4),
+                                "selection": "group-shared (one kept set per KV head)"}
+    # bulk (prefill) append of the whole context into an empty cache: the key
+    # transform (one fp32 FMA chain of d products per output), quantize and pack
     ctx = int(wl.ctx[0])
+    counts = torch.full((wl.batch,), ctx, dtype=torch.int32, device=qp.device)
+    fresh = M.Cache(wl.batch, wl.hkv, wl.d, wl.cap)
+    ts = []
+    for _ in range(4):
+        for t in fresh.planes().values():
+            t.zero_()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        M.transform_quantize_append(fresh, k_d, v_d, b_d, counts)
+        e1.record()
+        ts.append((e0, e1))
+    torch.cuda.synchronize()
+    us = float(np.mean([x.elapsed_time(y) for x, y in ts[1:]])) * 1e3
+    fma = wl.batch * wl.hkv * ctx * wl.d * wl.d
+    moved = (2 * wl.batch * wl.hkv * ctx * wl.d * 2 + wl.hkv * wl.d * wl.d * 4
+             + sum(M.cache_plane_bytes(wl.batch, wl.hkv, wl.d, ctx)[:6]))
+    res["bulk_append_128k"] = {"us": round(us, 1), "GB/s": round(moved / us / 1e3, 1),
+                               "bytes": int(moved), "fma": int(fma),
+                               "TFLOP/s": round(2 * fma / us / 1e6, 2),
+                               "frac_of_fp32_vector_157.3": round(2 * fma / us / 1e6 / 157.3, 4),
+                               "what": (f"{wl.batch}x{wl.hkv} units x {ctx} tokens appended in one "
+                                        "call: bf16 k, v in; k' = k B (fp32 FMA chains); INT2 planes out")}
+    # growing a full cache into a larger one (every plane re-strided)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    grown = M.cache_grow(fresh, wl.cap + 32768)
+    t1.record()
+    torch.cuda.synchronize()
+    gus = t0.elapsed_time(t1) * 1e3
+    gbytes = 2 * fresh.nbytes()
+    res["cache_grow"] = {"us_incl_zero_fill": round(gus, 1),
+                         "GB/s_incl_zero_fill": round((gbytes + grown.nbytes()) / gus / 1e3, 1),
+                         "from_cap": wl.cap, "to_cap": wl.cap + 32768}
+    del fresh, grown
+    torch.cuda.empty_cache()
+    # unpruned bf16 decode over the raw cache (2 copies rotate: 537 MB each)
     k2, v2 = k_d.clone(), v_d.clone()
     pairs = [(k_d, v_d), (k2, v2)]
     lengths = torch.full((wl.batch,), ctx, dtype=torch.int32, device=qp.device)
@@ -570,6 +656,23 @@ def stream_peak(M, torch, mib: int = 4096, reps: int = 10):
         e1.record()
         torch.cuda.synchronize()
         res[f"{name}_GB/s"] = round(moved * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    # the probe's launch shape swept: workgroups x 16-byte loads in flight per thread
+    sweep = {}
+    for wg in (256, 512, 1024, 2048):
+        for lif in (1, 2, 4, 8, 16):
+            M.stream_read_config(x, wg, lif, sink)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(4):
+                M.stream_read_config(x, wg, lif, sink)
+            e1.record()
+            torch.cuda.synchronize()
+            sweep[f"{wg}x{lif}"] = round(4 * 4 * n / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    best = max(sweep, key=sweep.get)
+    res["read_sweep_GB/s"] = sweep
+    res["read_best"] = {"config": best + " (workgroups x loads in flight)", "GB/s": sweep[best]}
+    res["read_GB/s"] = max(res["read_GB/s"], sweep[best])
     del x, y
     torch.cuda.empty_cache()
     log(f"stream peak: {res}")

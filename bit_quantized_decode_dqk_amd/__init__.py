@@ -34,7 +34,7 @@ _lib = None
 EXPORTS = ("dqk_status_str", "dqk_keep_count", "dqk_cache_plane_bytes", "dqk_transform_quantize_append",
            "dqk_select_channels", "dqk_append_select", "dqk_decode_workspace_bytes",
            "dqk_decode_attention", "dqk_select_channels_shared", "dqk_decode_attention_shared",
-           "dqk_decode_attention_noalloc",
+           "dqk_decode_attention_noalloc", "dqk_cache_grow", "dqk_stream_read_config",
            "dqk_dequant_reference", "dqk_bf16_decode_workspace_bytes",
            "dqk_bf16_decode_attention", "dqk_debug_f16_from_f32", "dqk_stream_read")
 
@@ -63,10 +63,12 @@ def lib():
             "dqk_decode_attention_shared": [C.POINTER(_Cache), P, P, I, I, C.c_float, I, P, P, S,
                                             P],
             "dqk_dequant_reference": [C.POINTER(_Cache), P, P, P],
+            "dqk_cache_grow": [C.POINTER(_Cache), C.POINTER(_Cache), P],
             "dqk_bf16_decode_workspace_bytes": [I, I, I, I, I, I, P],
             "dqk_bf16_decode_attention": [P, P, P, P, I, I, I, I, I, C.c_float, I, P, P, S, P],
             "dqk_debug_f16_from_f32": [P, P, S, P],
             "dqk_stream_read": [P, S, P, P],
+            "dqk_stream_read_config": [P, S, P, I, I, P],
         }.items():
             fn = getattr(L, name)
             fn.restype = C.c_int
@@ -304,6 +306,18 @@ def decode_attention_shared(cache: Cache, q_prime, sel_idx, sm_scale: float,
     return out
 
 
+def cache_grow(cache: Cache, capacity: int, stream=None) -> Cache:
+    """A new cache of a larger capacity (zero-filled, then dqk_cache_grow copies
+    every plane of `cache` into it): the same contents, room for more tokens."""
+    if capacity < cache.cap:
+        raise DqkError("a grown cache needs at least the old capacity")
+    dev = cache.k_codes.device
+    new = Cache(cache.batch, cache.hkv, cache.d, capacity, device=dev)
+    src, dst = cache.struct(), new.struct()
+    _check(lib().dqk_cache_grow(C.byref(src), C.byref(dst), _stream(stream)), "dqk_cache_grow")
+    return new
+
+
 def dequant_reference(cache: Cache, stream=None):
     """Dense dequantized keys and values [batch][hkv][capacity][d] fp32 (zero past each
     row's length): a checking and inspection aid, not on the decode path."""
@@ -372,4 +386,15 @@ def stream_read(buf, sink=None, stream=None):
         sink = torch.empty(STREAM_READ_SINK_WORDS, dtype=torch.int32, device=buf.device)
     _check(lib().dqk_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
                                  _stream(stream)), "dqk_stream_read")
+    return sink
+
+
+def stream_read_config(buf, workgroups: int, loads_in_flight: int, sink=None, stream=None):
+    """The read probe with its launch shape given (dqk_stream_read_config)."""
+    torch = _torch()
+    if sink is None:
+        sink = torch.empty(STREAM_READ_SINK_WORDS, dtype=torch.int32, device=buf.device)
+    _check(lib().dqk_stream_read_config(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                        int(workgroups), int(loads_in_flight), _stream(stream)),
+           "dqk_stream_read_config")
     return sink

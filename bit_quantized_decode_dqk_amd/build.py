@@ -35,6 +35,7 @@ SOURCES = {
     "dqk_combine.hip": [],
     "dqk_probe.hip": [],
     "dqk_noalloc.hip": [],
+    "dqk_grow.hip": [],
 }
 
 COMMON = ["-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -241,6 +241,37 @@ dqk_status dqk_decode_attention_shared(const dqk_cache *cache, const float *q_pr
                      ws_bytes, stream);
 }
 
+dqk_status dqk_cache_grow(const dqk_cache *src, const dqk_cache *dst, dqk_stream_t stream) {
+  dqk_status st = check_cache(src);
+  if (st != DQK_OK) return st;
+  st = check_cache(dst);
+  if (st != DQK_OK) return st;
+  if (src->batch != dst->batch || src->num_kv_heads != dst->num_kv_heads ||
+      src->head_dim != dst->head_dim || dst->capacity < src->capacity)
+    return DQK_ERR_INVALID;
+  // the two caches' planes must not overlap
+  const size_t units = (size_t)src->batch * src->num_kv_heads, d = (size_t)src->head_dim;
+  auto apart = [](const void *a, size_t na, const void *b, size_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x + na <= y || y + nb <= x;
+  };
+  const size_t cs = (size_t)src->capacity, cd = (size_t)dst->capacity;
+  const void *sp[] = {src->k_codes, src->k_scales, src->k_ch0, src->k_tail, src->v_codes,
+                      src->v_scales, src->lengths};
+  const void *dp[] = {dst->k_codes, dst->k_scales, dst->k_ch0, dst->k_tail, dst->v_codes,
+                      dst->v_scales, dst->lengths};
+  const size_t sn[] = {units * d * (cs / 4), units * d * (cs / 32) * 2, units * cs * 2,
+                       units * 32 * d * 4, units * (cs / 16) * d * 4, units * cs * (d / 32) * 2,
+                       (size_t)src->batch * 8};
+  const size_t dn[] = {units * d * (cd / 4), units * d * (cd / 32) * 2, units * cd * 2,
+                       units * 32 * d * 4, units * (cd / 16) * d * 4, units * cd * (d / 32) * 2,
+                       (size_t)dst->batch * 8};
+  for (int i = 0; i < 7; ++i)
+    for (int j = 0; j < 7; ++j)
+      if (!apart(sp[i], sn[i], dp[j], dn[j])) return DQK_ERR_INVALID;
+  return from_hip(dqk::launch_cache_grow(*src, *dst, reinterpret_cast<hipStream_t>(stream)));
+}
+
 dqk_status dqk_dequant_reference(const dqk_cache *cache, float *k_out, float *v_out,
                                  dqk_stream_t stream) {
   dqk_status st = check_cache(cache);
@@ -284,7 +315,21 @@ dqk_status dqk_debug_f16_from_f32(const float *x, uint16_t *out, size_t n, dqk_s
 dqk_status dqk_stream_read(const void *buf, size_t bytes, uint32_t *sink, dqk_stream_t stream) {
   if (!sink || !aligned16(sink) || bytes % 16 != 0) return DQK_ERR_INVALID;
   if (bytes > 0 && (!buf || !aligned16(buf))) return DQK_ERR_INVALID;
-  return from_hip(dqk::launch_stream_read(buf, bytes, sink, reinterpret_cast<hipStream_t>(stream)));
+  return from_hip(dqk::launch_stream_read(buf, bytes, sink, dqk::kStreamReadSinkWords / 4, 4,
+                                          reinterpret_cast<hipStream_t>(stream)));
+}
+
+dqk_status dqk_stream_read_config(const void *buf, size_t bytes, uint32_t *sink,
+                                  int32_t workgroups, int32_t loads_in_flight,
+                                  dqk_stream_t stream) {
+  if (!sink || !aligned16(sink) || bytes % 16 != 0) return DQK_ERR_INVALID;
+  if (bytes > 0 && (!buf || !aligned16(buf))) return DQK_ERR_INVALID;
+  if (workgroups < 1 || workgroups > dqk::kStreamReadSinkWords / 4) return DQK_ERR_INVALID;
+  if (loads_in_flight != 1 && loads_in_flight != 2 && loads_in_flight != 4 &&
+      loads_in_flight != 8 && loads_in_flight != 16)
+    return DQK_ERR_INVALID;
+  return from_hip(dqk::launch_stream_read(buf, bytes, sink, workgroups, loads_in_flight,
+                                          reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -92,6 +92,8 @@ hipError_t launch_decode4(const dqk_cache &c, const float *q_prime, const int32_
                           bool shared, int hq, int keep, float scale2, int split, bool even,
                           float *ws, hipStream_t s);
 hipError_t launch_dequant(const dqk_cache &c, float *k_out, float *v_out, hipStream_t s);
+// every plane of src re-strided into dst (same batch, KV heads, head_dim; larger capacity)
+hipError_t launch_cache_grow(const dqk_cache &src, const dqk_cache &dst, hipStream_t s);
 hipError_t launch_bf16_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                               const int32_t *lengths, int batch, int hq, int hkv, int d, int ld_t,
                               float sm_scale, int split, float *out, float *ws, hipStream_t s);
@@ -99,7 +101,9 @@ hipError_t launch_combine(const float *ws, int batch, int hq, int hkv, int d, in
                           float *out, hipStream_t s);
 hipError_t launch_f16_convert(const float *x, uint16_t *out, size_t n, hipStream_t s);
 constexpr int kStreamReadSinkWords = DQK_STREAM_READ_SINK_WORDS;   // 2048 workgroups x 4 wavefronts
-hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t s);
+// workgroups of 256 threads (1 .. kStreamReadSinkWords / 4), loads_in_flight in {1, 2, 4, 8, 16}
+hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, int workgroups,
+                              int loads_in_flight, hipStream_t s);
 
 // Device scratch of the decode entry point that allocates nothing: the split
 // partials of one call, at most kScratchBytes (one file-scope device array per

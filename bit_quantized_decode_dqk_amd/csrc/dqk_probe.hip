@@ -10,12 +10,12 @@ namespace {
 typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 
 constexpr int kThreadsR = 256;
-constexpr int kUnrollR = 4;   // loads in flight per thread and iteration
 
 // Thread i of the grid reads elements i, i + S, i + 2S, ... (S = grid threads),
-// four per iteration, XOR-folds them, and each wavefront leaves the XOR of its
-// lanes in sink[workgroup * 4 + wave]: the XOR of the whole sink is the XOR of
-// every 32-bit word of the buffer.
+// U per iteration (U loads in flight), XOR-folds them, and each wavefront
+// leaves the XOR of its lanes in sink[workgroup * 4 + wave]: the XOR of the
+// sink's first 4 * gridDim words is the XOR of every 32-bit word of the buffer.
+template <int kUnrollR>
 __global__ __launch_bounds__(kThreadsR) void stream_read_kernel(const u32x4v *__restrict__ p,
                                                                 size_t n, uint32_t *__restrict__ sink) {
   const size_t stride = (size_t)gridDim.x * kThreadsR;
@@ -37,10 +37,19 @@ __global__ __launch_bounds__(kThreadsR) void stream_read_kernel(const u32x4v *__
 
 }  // namespace
 
-hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t s) {
-  const unsigned grid = kStreamReadSinkWords / (kThreadsR / 64);
-  hipLaunchKernelGGL(stream_read_kernel, dim3(grid), dim3(kThreadsR), 0, s,
-                     static_cast<const u32x4v *>(buf), bytes / 16, sink);
+hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, int workgroups,
+                              int loads_in_flight, hipStream_t s) {
+  const dim3 grid((unsigned)workgroups), block(kThreadsR);
+  const u32x4v *p = static_cast<const u32x4v *>(buf);
+  const size_t n = bytes / 16;
+  switch (loads_in_flight) {
+    case 1: hipLaunchKernelGGL(stream_read_kernel<1>, grid, block, 0, s, p, n, sink); break;
+    case 2: hipLaunchKernelGGL(stream_read_kernel<2>, grid, block, 0, s, p, n, sink); break;
+    case 4: hipLaunchKernelGGL(stream_read_kernel<4>, grid, block, 0, s, p, n, sink); break;
+    case 8: hipLaunchKernelGGL(stream_read_kernel<8>, grid, block, 0, s, p, n, sink); break;
+    case 16: hipLaunchKernelGGL(stream_read_kernel<16>, grid, block, 0, s, p, n, sink); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -224,6 +224,20 @@ dqk_status dqk_decode_attention_shared(const dqk_cache *cache, const float *q_pr
                                        void *workspace, size_t workspace_bytes,
                                        dqk_stream_t stream);
 
+/* Growing a cache: the cache grows with every generated token (tech.dede.sh
+ * summary, "Why the cache becomes a bottleneck"), and a sequence that outgrows
+ * the capacity its cache was created with moves to a larger one.  Copies every
+ * plane of src into dst, which has the same batch, num_kv_heads and head_dim and
+ * capacity >= src's: each unit's rows of src go to the start of dst's rows, and
+ * the lengths plane (lengths and arrival counters) is copied whole.  Nothing
+ * stored depends on the capacity, so when dst's planes were zero-filled the
+ * result is byte for byte the cache that the same appends would have built at
+ * dst's capacity; later appends and decodes on dst continue as on src.  dst's
+ * positions past src's capacity keep their contents.  Must not run concurrently
+ * with an append to src.  Errors: DQK_ERR_INVALID for an invalid cache, shapes
+ * that differ, a smaller dst capacity, or planes of src and dst that overlap. */
+dqk_status dqk_cache_grow(const dqk_cache *src, const dqk_cache *dst, dqk_stream_t stream);
+
 /* Dense dequantized cache for checking and inspection: k_out, v_out
  * [batch][hkv][capacity][d] fp32 hold k~ and v~ as defined above for t < len and
  * zero past it.  Not on the decode path. */
@@ -264,6 +278,17 @@ dqk_status dqk_debug_f16_from_f32(const float *x, uint16_t *out, size_t n,
  * pointers or sizes. */
 #define DQK_STREAM_READ_SINK_WORDS 8192
 dqk_status dqk_stream_read(const void *buf, size_t bytes, uint32_t *sink, dqk_stream_t stream);
+
+/* The same probe with its launch shape as arguments, for a sweep of the read
+ * rate: `workgroups` workgroups of 256 threads (1 .. DQK_STREAM_READ_SINK_WORDS/4;
+ * dqk_stream_read uses the maximum) and loads_in_flight 16-byte loads per thread
+ * and iteration (1, 2, 4, 8 or 16; dqk_stream_read uses 4).  The XOR of the first
+ * 4 * workgroups sink words equals the XOR of the buffer's 32-bit words; the other
+ * sink words are not written.  Errors: DQK_ERR_INVALID as dqk_stream_read, or for
+ * a launch shape outside these ranges. */
+dqk_status dqk_stream_read_config(const void *buf, size_t bytes, uint32_t *sink,
+                                  int32_t workgroups, int32_t loads_in_flight,
+                                  dqk_stream_t stream);
 
 #ifdef __cplusplus
 }

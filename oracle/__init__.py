@@ -72,6 +72,7 @@ def _declare(L):
     L.dqko_queries_shared.argtypes = [P, P, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, P, P]
     L.dqko_append.argtypes = [C.POINTER(_Cache), P, P, P, P, C.c_int32]
     L.dqko_dequant.argtypes = [C.POINTER(_Cache), P, P]
+    L.dqko_cache_grow.argtypes = [C.POINTER(_Cache), C.POINTER(_Cache)]
     L.dqko_attend_dense.argtypes = [P, P, C.c_int, P, P, C.c_int, C.c_int, C.c_ssize_t,
                                     C.c_double, P]
     L.dqko_decode.argtypes = [C.POINTER(_Cache), P, P, C.c_int, C.c_int, C.c_double, P, P,
@@ -203,6 +204,14 @@ class Cache:
         n = np.ascontiguousarray(n_new, dtype=np.int32)
         s = self._struct()
         lib().dqko_append(C.byref(s), _p(k_new), _p(v_new), _p(bm), _p(n), max_new)
+
+    def grow(self, cap: int) -> "Cache":
+        """A cache of capacity `cap` (>= this one's) holding the same contents."""
+        assert cap >= self.cap and cap % 32 == 0
+        out = Cache(self.batch, self.hkv, self.d, cap)
+        s, t = self._struct(), out._struct()
+        lib().dqko_cache_grow(C.byref(s), C.byref(t))
+        return out
 
     def dequant(self):
         k = np.zeros((self.batch, self.hkv, self.cap, self.d), dtype=np.float32)

@@ -334,6 +334,31 @@ void dqko_append(const dqko_cache *c, const float *k_new, const float *v_new,
     free(kp);
 }
 
+/* The cache grows with every generated token (tech.dede.sh summary, "Why the
+ * cache becomes a bottleneck"); a sequence that outgrows its capacity moves to a
+ * larger cache.  Every stored element keeps its (unit, channel, token) place:
+ * element by element, each plane of src is copied to the same indices of dst. */
+void dqko_cache_grow(const dqko_cache *src, const dqko_cache *dst)
+{
+    const int d = src->d;
+    for (int b = 0; b < src->batch; ++b) {
+        for (int g = 0; g < src->hkv; ++g) {
+            for (int ch = 0; ch < d; ++ch) {
+                for (int i = 0; i < src->cap / 4; ++i) kc_row(dst, b, g, ch)[i] = kc_row(src, b, g, ch)[i];
+                for (int i = 0; i < src->cap / 32; ++i) ks_row(dst, b, g, ch)[i] = ks_row(src, b, g, ch)[i];
+            }
+            for (int t = 0; t < src->cap; ++t) {
+                ch0_row(dst, b, g)[t] = ch0_row(src, b, g)[t];
+                for (int j = 0; j < d / 32; ++j) vs_row(dst, b, g, t)[j] = vs_row(src, b, g, t)[j];
+            }
+            for (int t = 0; t < src->cap; t += 16)
+                for (int ch = 0; ch < d; ++ch) *vword(dst, b, g, t, ch) = *vword(src, b, g, t, ch);
+            for (int i = 0; i < 32 * d; ++i) tail_of(dst, b, g)[i] = tail_of(src, b, g)[i];
+        }
+        dst->lengths[b] = src->lengths[b];
+    }
+}
+
 /* ------------------------------------------------------------- dequant */
 
 void dqko_dequant(const dqko_cache *c, float *k_out, float *v_out)

@@ -100,6 +100,10 @@ void dqko_queries_shared(const float *q, const float *a, int batch, int hq, int 
 void dqko_append(const dqko_cache *c, const float *k_new, const float *v_new,
                  const float *bm, const int32_t *n_new, int32_t max_new);
 
+/* Copy every stored element of src to the same (unit, channel, token) place of
+ * dst, whose batch, hkv and d are src's and whose cap is at least src's. */
+void dqko_cache_grow(const dqko_cache *src, const dqko_cache *dst);
+
 /* Dense dequantized cache: k_out, v_out [batch][hkv][cap][d]; zero past lengths. */
 void dqko_dequant(const dqko_cache *c, float *k_out, float *v_out);
 

@@ -147,6 +147,23 @@ def test_noalloc_decode_validation_without_gpu():
     assert L.dqk_decode_attention_noalloc(big, q, idx, 32, 77, 0.1, 256, out, None) == WORKSPACE
 
 
+def test_cache_grow_validation_without_gpu():
+    """dqk_cache_grow refuses differing shapes, a smaller destination and planes
+    that overlap, before anything is launched."""
+    L = M.lib()
+    src = fake_cache()
+    far = {n: 0x1000000 * (i + 1) for i, n in enumerate(M.PLANES)}
+    dst = fake_cache(capacity=512, **far)
+    assert L.dqk_cache_grow(None, C.byref(dst), None) == INVALID
+    assert L.dqk_cache_grow(C.byref(src), None, None) == INVALID
+    assert L.dqk_cache_grow(C.byref(src), C.byref(fake_cache(capacity=128, **far)), None) == INVALID
+    assert L.dqk_cache_grow(C.byref(src), C.byref(fake_cache(capacity=512, batch=3, **far)), None) == INVALID
+    assert L.dqk_cache_grow(C.byref(src), C.byref(fake_cache(capacity=512, num_kv_heads=1, **far)), None) == INVALID
+    assert L.dqk_cache_grow(C.byref(src), C.byref(fake_cache(capacity=512, head_dim=64, **far)), None) == INVALID
+    assert L.dqk_cache_grow(C.byref(src), C.byref(fake_cache(capacity=512)), None) == INVALID   # same planes
+    assert L.dqk_cache_grow(C.byref(src), C.byref(fake_cache(capacity=100, **far)), None) == INVALID
+
+
 def test_stream_read_validation_without_gpu():
     """The read probe rejects null or misaligned pointers and sizes that are not
     whole 16-byte elements before launching anything."""
@@ -157,6 +174,17 @@ def test_stream_read_validation_without_gpu():
     assert L.dqk_stream_read(buf, (1 << 20) + 8, sink, None) == INVALID
     assert L.dqk_stream_read(None, 1 << 20, sink, None) == INVALID
     assert L.dqk_stream_read(buf + 8, 1 << 20, sink, None) == INVALID
+
+
+def test_stream_read_config_validation_without_gpu():
+    L = M.lib()
+    buf, sink = 0x20000, 0x30000
+    assert L.dqk_stream_read_config(buf, 1 << 20, sink, 0, 4, None) == INVALID
+    assert L.dqk_stream_read_config(buf, 1 << 20, sink, 2049, 4, None) == INVALID
+    assert L.dqk_stream_read_config(buf, 1 << 20, sink, 256, 3, None) == INVALID
+    assert L.dqk_stream_read_config(buf, 1 << 20, sink, 256, 32, None) == INVALID
+    assert L.dqk_stream_read_config(buf + 8, 1 << 20, sink, 256, 4, None) == INVALID
+    assert L.dqk_stream_read_config(buf, 1 << 20, None, 256, 4, None) == INVALID
 
 
 def test_append_select_dequant_validation_without_gpu():

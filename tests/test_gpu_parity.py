@@ -678,6 +678,20 @@ def test_stream_read_folds_every_word(nbytes):
     assert got == want, (nbytes, hex(int(got)), hex(int(want)))
 
 
+@pytest.mark.parametrize("wg,lif", [(1, 1), (256, 16), (1000, 8), (2048, 2)])
+def test_stream_read_config_folds_every_word(wg, lif):
+    """The probe with a given launch shape reads each 16-byte element once: the
+    XOR of the sink words it writes equals the XOR of the buffer's words."""
+    nbytes = (8 << 20) + 16 * 333
+    words = np.random.default_rng(wg + lif).integers(0, 1 << 32, size=nbytes // 4,
+                                                     dtype=np.uint64).astype(np.uint32)
+    buf = torch.from_numpy(words.view(np.int32)).cuda()
+    sink = torch.zeros((M.STREAM_READ_SINK_WORDS,), dtype=torch.int32, device="cuda")
+    M.stream_read_config(buf, wg, lif, sink)
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32)[:4 * wg])
+    assert got == np.bitwise_xor.reduce(words), (wg, lif)
+
+
 @pytest.mark.parametrize("lens,sm_mult", [([4096], 1.0), ([4096], 0.02), ([1000, 1, 0, 2049], 0.05)])
 def test_bf16_decode_matches_plain_attention(orc, lens, sm_mult):
     wl = W.custom("bf16cmp", 26, len(lens), 32, 8, 128, lens, 4096 + 64, "bf16",
@@ -777,3 +791,35 @@ def test_decode_shared_matches_oracle(orc, hq, hkv, d, cap, lens):
         for out in outs:
             assert not out[lens.index(0)].any()
     decode_shared_case(orc, wl, sparsity=60, sm_mult=0.05)
+
+
+# ----------------------------------------------------------------------------- growing a cache
+
+@pytest.mark.parametrize("d,cap0,cap1,lens", [(128, 96, 224, [90, 33]), (64, 1024, 1344, [1000, 0, 517]),
+                                               (128, 4096, 8192, [4095, 4096])])
+def test_cache_grow_matches_oracle(orc, d, cap0, cap1, lens):
+    """dqk_cache_grow against the oracle's element-wise copy, byte for byte; then
+    appends on the grown cache (closing the unfinished groups and passing the
+    old capacity) and a decode, against the oracle doing the same."""
+    wl = W.custom(f"grow{d}-{cap0}", 53, len(lens), 4 * (d // 64), d // 64, d, lens, cap0, "bf16",
+                  log_uniform_key_scales=True)
+    g, a, b, k, v = build_gpu(wl)
+    ref = build_oracle(orc, wl, k, v, b)
+    big = M.cache_grow(g, cap1)
+    ref_big = ref.grow(cap1)
+    say("grow", wl.describe(), "->", cap1)
+    assert_same_cache(planes_np(big), ref_big)
+    n = cap1 - cap0 - 40
+    more = W.round_bf16(np.random.default_rng(54).standard_normal((wl.batch, wl.hkv, n, d)).astype(np.float32))[0]
+    counts = np.array([n, 37, 1][:wl.batch], dtype=np.int32)
+    M.transform_quantize_append(big, dev_input(more, "bf16"), dev_input(more, "bf16"), dev_f32(b), dev_i32(counts))
+    ref_big.append(more, more, b, list(counts))
+    assert_same_cache(planes_np(big), ref_big)
+    keep = orc.keep_count(d, 40)
+    q = W.queries(wl)
+    qp, idx = gpu_queries(wl, q, a, keep)
+    qpo, idxo = orc.queries(q, a, wl.hkv, keep)
+    sm = W.default_sm_scale(d)
+    err = rel_err(M.decode_attention(big, qp, idx, sm).cpu().numpy(), ref_big.decode(qpo, idxo, sm))
+    say(f"  decode after grow and append: max rel err {err:.3e}")
+    assert err <= REL_TOL

@@ -724,3 +724,47 @@ def test_queries_shared_groups(orc):
             rows = qp1[bb, g * wl.group:(g + 1) * wl.group]
             assert np.array_equal(idx[bb, g], orc.select_shared(rows, 77))
     assert orc.per_head(idx, wl.group).shape == (2, wl.hq, 77)
+
+
+# ----------------------------------------------------------------------------- growing a cache
+
+def test_grow_then_append_equals_building_large(orc):
+    """Nothing stored depends on the capacity: a cache built at capacity 96,
+    grown to 224 and appended to is byte for byte the cache the same appends
+    build at capacity 224 (ragged rows, an unfinished key group at the grow, a
+    group closed after it), and it decodes to the same output."""
+    wl = W.custom("grow", 50, 2, 8, 2, 128, [90, 33], 224, "bf16", log_uniform_key_scales=True)
+    a, b = W.transforms(wl)
+    k, v = W.prefill_kv(wl)
+    small = orc.Cache(2, 2, 128, 96)
+    small.append(k[:, :, :90], v[:, :, :90], b, [90, 33])
+    grown = small.grow(224)
+    assert list(grown.lengths) == [90, 33]
+    big = orc.Cache(2, 2, 128, 224)
+    big.append(k[:, :, :90], v[:, :, :90], b, [90, 33])
+    rng = np.random.default_rng(51)
+    more = W.round_bf16(rng.standard_normal((2, 2, 100, 128)).astype(np.float32))[0]
+    grown.append(more, more, b, [100, 7])
+    big.append(more, more, b, [100, 7])
+    for name, arr in big.planes().items():
+        g = grown.planes()[name]
+        if name == "k_tail":
+            for bb in range(2):
+                r = int(big.lengths[bb]) % 32
+                assert np.array_equal(g[bb, :, :r], arr[bb, :, :r])
+        else:
+            assert np.array_equal(g, arr), name
+    qp, idx = orc.queries(W.queries(wl), a, 2, 77)
+    sm = W.default_sm_scale(128)
+    assert np.array_equal(grown.decode(qp, idx, sm).view(np.uint32), big.decode(qp, idx, sm).view(np.uint32))
+
+
+def test_grow_same_capacity_is_a_copy(orc):
+    wl = W.custom("grow2", 52, 1, 4, 1, 64, [70], 96, "f32")
+    _, b = W.transforms(wl)
+    k, v = W.prefill_kv(wl)
+    c = orc.Cache(1, 1, 64, 96)
+    c.append(k[:, :, :70], v[:, :, :70], b, [70])
+    g = c.grow(96)
+    for name, arr in c.planes().items():
+        assert np.array_equal(g.planes()[name], arr), name
