@@ -82,6 +82,7 @@ def append_bytes(batch: int, hkv: int, d: int, positions, in_bytes: int) -> int:
 
 KERNEL_SOURCES = ("bit_quantized_decode_dqk_amd/csrc/dqk_decode.hip",
                   "bit_quantized_decode_dqk_amd/csrc/dqk_decode4.hip",
+                  "bit_quantized_decode_dqk_amd/csrc/dqk_decode_ops.h",
                   "bit_quantized_decode_dqk_amd/csrc/dqk_combine.hip",
                   "bit_quantized_decode_dqk_amd/csrc/dqk_wave.h",
                   "bit_quantized_decode_dqk_amd/csrc/dqk_internal.h")
@@ -272,6 +273,8 @@ def main():
     ap.add_argument("--summarize-rocprof", metavar="DIR",
                     help="print a summary of rocprofv3 csv output under DIR and exit")
     ap.add_argument("--kernel-regex", default="decode_kernel")
+    ap.add_argument("--only-workload", choices=("tiny", "gqa8k", "append32k", "ragged64k"),
+                    help="time only this other workload's steps (for a profiler run) and exit")
     args = ap.parse_args()
     if args.summarize_rocprof:
         summarize_rocprof(args.summarize_rocprof, args.kernel_regex, args.calibrate_copy_mib)
@@ -286,6 +289,9 @@ def main():
     import bit_quantized_decode_dqk_amd as M
 
     torch.cuda.set_device(0)
+    if args.only_workload:
+        print(json.dumps(run_configs(M, torch, names=(args.only_workload,))), flush=True)
+        return
     dev = "cuda"
     wl = W.workload("ctx128k", steps=256)
     keep = M.keep_for_sparsity(wl.d, args.sparsity)
@@ -679,7 +685,7 @@ def stream_peak(M, torch, mib: int = 4096, reps: int = 10):
     return res
 
 
-def run_configs(M, torch, steps: int = 32):
+def run_configs(M, torch, steps: int = 32, names=("tiny", "gqa8k", "append32k", "ragged64k")):
     """The other workloads, one step each as on the 128K line: select + decode (the
     tiny G = 1 case, GQA 32/8 at 8K, the ragged batch of 16 with G = 8) or the fused
     append-1 + select, then decode (the 32K append loop, 64 steps).  Queries follow
@@ -689,7 +695,7 @@ def run_configs(M, torch, steps: int = 32):
     captured HIP graph of its steps, replayed once untimed and once timed."""
     dev = "cuda"
     res = {}
-    for name in ("tiny", "gqa8k", "append32k", "ragged64k"):
+    for name in names:
         t0 = time.time()
         wl = W.workload(name)
         appends = wl.steps > 0
