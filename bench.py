@@ -452,6 +452,7 @@ def main():
         extras = run_extras(M, torch, wl, caches, a_d, b_d, step_q, qp, idx, out, ws, k_d, v_d,
                             sm, args, roof_us)
         extras["other_workloads"] = run_configs(M, torch)
+        extras["transform_fit"] = transform_fit_report(M, torch)
         extras["stream_peak"] = stream_peak(M, torch)
 
     result = {
@@ -497,6 +498,73 @@ def main():
         log("timing the CPU oracle on a bounded sample ...")
         result["cpu_baseline"] = cpu_baseline(wl, a, b, keep, sm)
     print(json.dumps(result), flush=True)
+
+
+def transform_fit_report(M, torch, d: int = 128, n_keys: int = 8192, n_q: int = 256,
+                         sparsity: int = 40):
+    """The paired transforms fitted from covariances (calibrate.fit_transforms) against
+    a shared random rotation and no transform, on synthetic statistics: keys with the
+    workloads' per-channel scales (log-uniform 0.5..20, channel 0 x8), queries with a
+    decaying spectrum i^-1.5 in a random basis.  Keys pass through the library's own
+    append (transform, INT2 quantize) and dequant kernels; queries through its
+    selection kernel.  Reported per method: the share of |q'|^2 in the kept channels,
+    the relative error of the pruned logits (exact keys, then stored INT2 keys) against
+    q.k, and of the attention output against exact attention (fp64, host)."""
+    from bit_quantized_decode_dqk_amd import calibrate as CAL
+    rng = np.random.default_rng(np.random.SeedSequence([0, 6, 0]))
+    s = np.exp(rng.uniform(np.log(0.5), np.log(20.0), d))
+    s[0] *= 8.0
+    sk = np.diag(s ** 2)
+    v, _ = np.linalg.qr(rng.standard_normal((d, d)))
+    e = np.arange(1, d + 1, dtype=np.float64) ** -1.5
+    sq = (v * e) @ v.T
+    keys = (rng.standard_normal((n_keys, d)) * s).astype(np.float32)
+    vals = rng.standard_normal((n_keys, d)).astype(np.float32)
+    qs = (rng.standard_normal((n_q, d)) * np.sqrt(e)) @ v.T
+    qs = qs.astype(np.float32)
+    keep = M.keep_for_sparsity(d, sparsity)
+    sm = 1.0 / np.sqrt(d)
+    z_ex = qs.astype(np.float64) @ keys.astype(np.float64).T
+    nq_att = 64
+
+    def attend(z, vv):
+        z = z * sm
+        w = np.exp(z - z.max(axis=1, keepdims=True))
+        return (w @ vv) / w.sum(axis=1, keepdims=True)
+
+    o_ex = attend(z_ex[:nq_att], vals.astype(np.float64))
+    methods = {"dual_qk_alpha0.5": CAL.fit_transforms(sk, sq, 0.5)[:2],
+               "dual_qk_alpha1.0": CAL.fit_transforms(sk, sq, 1.0)[:2],
+               "shared_rotation": CAL.rotation_transforms(d, seed=5),
+               "identity": (np.eye(d, dtype=np.float32), np.eye(d, dtype=np.float32))}
+    out = {"keep": keep, "keys": n_keys, "queries": n_q,
+           "what": ("share of |q'|^2 kept; relative Frobenius error of pruned logits (exact k', "
+                    "stored INT2 k') and of attention outputs, against exact q.k attention")}
+    for name, (a, b) in methods.items():
+        cache = M.Cache(1, 1, d, n_keys)
+        kd = torch.from_numpy(keys).cuda().view(1, 1, n_keys, d)
+        vd = torch.from_numpy(vals).cuda().view(1, 1, n_keys, d)
+        M.transform_quantize_append(cache, kd, vd, torch.from_numpy(b).cuda()[None],
+                                    torch.tensor([n_keys], dtype=torch.int32, device="cuda"))
+        kq, vq = M.dequant_reference(cache)
+        # each query a batch row of one head over the one KV head
+        qp, idx = M.select_channels(torch.from_numpy(qs).cuda()[:, None].contiguous(),
+                                    torch.from_numpy(a).cuda()[None], 1, keep)
+        qp = qp[:, 0].double().cpu().numpy()
+        mask = np.zeros_like(qp)
+        np.put_along_axis(mask, idx[:, 0].long().cpu().numpy(), 1.0, axis=1)
+        qm = qp * mask
+        kexact = keys.astype(np.float64) @ b.astype(np.float64)
+        z_prune = qm @ kexact.T
+        z_int2 = qm @ kq[0, 0].double().cpu().numpy().T
+        e_kept = float(np.mean((qm ** 2).sum(1) / (qp ** 2).sum(1)))
+        rel = lambda z: float(np.linalg.norm(z - z_ex) / np.linalg.norm(z_ex))
+        o = attend(z_int2[:nq_att], vq[0, 0].double().cpu().numpy())
+        out[name] = {"energy_kept": round(e_kept, 4), "logit_err_pruned": round(rel(z_prune), 4),
+                     "logit_err_pruned_int2": round(rel(z_int2), 4),
+                     "attn_out_err_int2_pruned": round(float(np.linalg.norm(o - o_ex) / np.linalg.norm(o_ex)), 4)}
+        del cache
+    return out
 
 
 def pages_comparison(M, wl, extras, dec_us, dec_bytes):
