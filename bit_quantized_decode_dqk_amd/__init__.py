@@ -306,13 +306,16 @@ def decode_attention_shared(cache: Cache, q_prime, sel_idx, sm_scale: float,
     return out
 
 
-def cache_grow(cache: Cache, capacity: int, stream=None) -> Cache:
-    """A new cache of a larger capacity (zero-filled, then dqk_cache_grow copies
-    every plane of `cache` into it): the same contents, room for more tokens."""
+def cache_grow(cache: Cache, capacity: int, out: Optional[Cache] = None, stream=None) -> Cache:
+    """A cache of a larger capacity holding the same contents (dqk_cache_grow copies
+    every plane of `cache` into it): `out` if given (zero-filled by the caller),
+    else a new zero-filled cache."""
     if capacity < cache.cap:
         raise DqkError("a grown cache needs at least the old capacity")
-    dev = cache.k_codes.device
-    new = Cache(cache.batch, cache.hkv, cache.d, capacity, device=dev)
+    new = out if out is not None else Cache(cache.batch, cache.hkv, cache.d, capacity,
+                                            device=cache.k_codes.device)
+    if (new.batch, new.hkv, new.d, new.cap) != (cache.batch, cache.hkv, cache.d, capacity):
+        raise DqkError("the destination cache has another shape")
     src, dst = cache.struct(), new.struct()
     _check(lib().dqk_cache_grow(C.byref(src), C.byref(dst), _stream(stream)), "dqk_cache_grow")
     return new
