@@ -122,6 +122,7 @@ struct __attribute__((aligned(16))) Smem4 {
     uint32_t w[kG4 * D / 4];
   } kept;
   unsigned long long umask[2];   // the union U of kept key channels >= 1: bit c of word c / 64
+  int32_t ulist[D];              // compact slots: key channel of slot i (-1 past |U|)
 };
 
 // Registers of one block of keys in flight.
@@ -139,12 +140,16 @@ struct VStage4 {
   uint32_t vs[Lay4<D>::VG];      // value scales of tokens t, t+1: [t groups | t+1 groups]
 };
 
-template <int D>
+// COMPACT (group-shared kept sets, one per KV head): union slot i holds the
+// i-th kept key channel other than 0, so the slots past |U| = keep - 1 fill
+// only the last of the nkc K chunks that are worked on; otherwise slot i holds
+// channel i + 1 and all K chunks run.
+template <int D, bool COMPACT>
 __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
                                                                const float *__restrict__ qp,
                                                                const int32_t *__restrict__ sel,
                                                                int shared, int hq, int keep, float scale2,
-                                                               int nsplit, int bps, int ncu,
+                                                               int nsplit, int bps, int ncu, int nkc,
                                                                float *__restrict__ ws) {
   using L = Lay4<D>;
   constexpr int G = kG4;
@@ -178,6 +183,11 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
     qv[k] = qp[row0 * D + e];
     // the head's kept set: its own row, or its KV head's shared one
     sv[k] = e < G * keep ? (shared ? sel[(size_t)unit * keep + e % keep] : sel[row0 * keep + e]) : -1;
+  }
+  // compact slots: the shared kept list without channel 0, one slot per lane
+  int uch = -1;
+  if constexpr (COMPACT) {
+    if (tid < D && tid + 1 < keep) uch = sel[(size_t)unit * keep + tid + 1];
   }
   const int len = max(0, min(c.lengths[b], c.capacity));
   const int nblk_all = (len + kBlock4 - 1) / kBlock4;
@@ -288,12 +298,6 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
   };
   const int lo = (tid >> 4) % L::OCT, lq = tid & 15;
   const uint32_t kc_row = (uint32_t)kc_stride, ks_row = 2u * (uint32_t)ks_stride;
-  uint32_t kvo[8];
-#pragma unroll
-  for (int cc = 0; cc < 8; ++cc) {
-    const int ch = 8 * lo + cc + 1;
-    kvo[cc] = ch < D ? mul_apart((uint32_t)ch, kc_row) + 4u * (uint32_t)lq : kFar;
-  }
   // logit A operands, built here from the key scales: job j (one per lane; the
   // upper lanes repeat the lower ones at head_dim 64) is key-group pair gp = tile
   // j % 4 of the block and union slots s0 = 8o + a, s1 = s0 + 2 (a = 0, 1, 4, 5),
@@ -301,9 +305,27 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
   const int aj = tid % (4 * L::SPJ), agp = aj & 3, asp = aj >> 2;
   const int aoct = asp >> 2, am = asp & 3;
   const int as0 = 8 * aoct + (am & 1) + 4 * (am >> 1), as1 = as0 + 2;
-  uint32_t ksv[2];
-  ksv[0] = as0 + 1 < D ? mul_apart((uint32_t)(as0 + 1), ks_row) + 4u * (uint32_t)agp : kFar;
-  ksv[1] = as1 + 1 < D ? mul_apart((uint32_t)(as1 + 1), ks_row) + 4u * (uint32_t)agp : kFar;
+  // a wavefront's key-code and A jobs are the 32 slots from 32 (wave mod OCT/4) on:
+  // with compact slots, a wavefront whose slots all lie past the nkc chunks has
+  // none to read or build (workgroup- and wavefront-uniform)
+  const bool slots_live = !COMPACT || 32 * (wave % (L::OCT / 4)) < 16 * nkc;
+  // channel of a slot: i + 1, or the compact list (LDS, filled in the setup)
+  auto slot_channel = [&](int i) -> int {
+    if constexpr (COMPACT) return sm.ulist[i];
+    else return i + 1 < D ? i + 1 : -1;
+  };
+  uint32_t kvo[8], ksv[2];
+  auto job_offsets = [&]() {
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc) {
+      const int ch = slot_channel(8 * lo + cc);
+      kvo[cc] = ch >= 0 && slots_live ? mul_apart((uint32_t)ch, kc_row) + 4u * (uint32_t)lq : kFar;
+    }
+    const int c0a = slot_channel(as0), c1a = slot_channel(as1);
+    ksv[0] = c0a >= 0 && slots_live ? mul_apart((uint32_t)c0a, ks_row) + 4u * (uint32_t)agp : kFar;
+    ksv[1] = c1a >= 0 && slots_live ? mul_apart((uint32_t)c1a, ks_row) + 4u * (uint32_t)agp : kFar;
+  };
+  if constexpr (!COMPACT) job_offsets();
   // channel 0: dword tid (tokens 2 tid, 2 tid + 1) for the lower 128 lanes
   const uint32_t c0o = tid < kBlock4 / 2 ? 4u * tid : kFar;
 
@@ -328,13 +350,20 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
 
   const int nbc0 = nb == kChunk4 + 1 ? kChunk4 + 1 : min(kChunk4, nb);
   KStage4<D> S0, S1;
-  kissue(S0, t_begin, 0 < nbc0);
+  if constexpr (!COMPACT) kissue(S0, t_begin, 0 < nbc0);
 
   // ---------------------------------------------------------------- setup (whole workgroup)
   // Barriers here order LDS only (block_barrier): a full __syncthreads would also
   // wait for the blocks just issued.
   for (int e = tid; e < G * D / 4; e += kThreads4) sm.kept.w[e] = 0u;
+  if constexpr (COMPACT) {
+    if (tid < D) sm.ulist[tid] = uch >= 1 && uch < D ? uch : -1;
+  }
   block_barrier();
+  if constexpr (COMPACT) {   // the first block once the compact slots are known
+    job_offsets();
+    kissue(S0, t_begin, 0 < nbc0);
+  }
 #pragma unroll
   for (int k = 0; k < SJ; ++k) {
     const int e = tid + kThreads4 * k;
@@ -392,13 +421,14 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
     sm.tailz[h][r] = zz;
   }
   // coefficients in slot order, scaled by 2^-E_h (E_h: exponent of the head's
-  // largest |coefficient| over channels >= 1); slot i is channel i + 1
+  // largest |coefficient| over channels >= 1)
   for (int e = tid; e < G * D; e += kThreads4) {
     const int h = e / D, i = e % D;
     const float mx = D > 64 ? fmaxf(sm.redm[h][0], sm.redm[h][1]) : sm.redm[h][0];
     int ex = 0;
     if (mx > 0.0f) frexpf(mx, &ex);
-    sm.coefs[h][i] = i + 1 < D ? sm.coefc[h][i + 1] * ldexpf(1.0f, -ex) : 0.0f;
+    const int ch = slot_channel(i);
+    sm.coefs[h][i] = ch >= 0 ? sm.coefc[h][ch] * ldexpf(1.0f, -ex) : 0.0f;
     if (i == 0) sm.e2[h] = ldexpf(1.0f, ex);
   }
   block_barrier();
@@ -414,13 +444,18 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
   uint32_t ksm[2];
   {
     // later blocks read the union's channels only
+    // (compact slots hold union channels only; past |U| they read nothing)
     const unsigned long long m0 = sm.umask[0], m1 = sm.umask[1];
-    auto member = [&](int ch) { return ((ch < 64 ? m0 >> ch : m1 >> (ch & 63)) & 1ull) != 0ull; };
+    auto member = [&](int slot) {
+      const int ch = slot_channel(slot);
+      if (ch < 1) return false;
+      return ((ch < 64 ? m0 >> ch : m1 >> (ch & 63)) & 1ull) != 0ull;
+    };
 #pragma unroll
     for (int cc = 0; cc < 8; ++cc)
-      if (!member(8 * lo + cc + 1)) kvo[cc] = kFar;
-    ksm[0] = member(as0 + 1) ? 0xffffffffu : 0u;
-    ksm[1] = member(as1 + 1) ? 0xffffffffu : 0u;
+      if (!member(8 * lo + cc)) kvo[cc] = kFar;
+    ksm[0] = member(as0) ? 0xffffffffu : 0u;
+    ksm[1] = member(as1) ? 0xffffffffu : 0u;
     if (!ksm[0]) ksv[0] = kFar;
     if (!ksm[1]) ksv[1] = kFar;
   }
@@ -429,7 +464,7 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
   kissue(S1, t_begin + kBlock4, 1 < nbc0);
 
   auto kcommit = [&](KStage4<D> &S, KBlock4<D> &B, int p0) {
-    {
+    if (slots_live) {
       uint32_t y0[4], y1[4];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
@@ -452,6 +487,7 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
     // tail or beyond) count as zero.  High part = fp16 of the product, low part =
     // fp16 of what the high part leaves out (about 22 significant bits together).
     uint32_t v0 = S.ks[0] & ksm[0], v1 = S.ks[1] & ksm[1];
+    if (slots_live) {
     if (p0 + kBlock4 > code_end) {   // workgroup-uniform
       const int g0 = p0 / kGroup + 2 * agp;
       const uint32_t km = (g0 * kGroup < code_end ? 0xffffu : 0u) | ((g0 + 1) * kGroup < code_end ? 0xffff0000u : 0u);
@@ -469,6 +505,7 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
       *reinterpret_cast<uint32_t *>(&ar[2 * h + 1][8 * aoct + 2 * am]) = lo0;
       *reinterpret_cast<uint32_t *>(&ar[8 + 2 * h][8 * aoct + 2 * am]) = hi1;
       *reinterpret_cast<uint32_t *>(&ar[8 + 2 * h + 1][8 * aoct + 2 * am]) = lo1;
+    }
     }
     B.c0w[tid] = S.c0;
   };
@@ -512,6 +549,9 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
       const int astep = arow ? 16 : 0;
 #pragma unroll
       for (int kc = 0; kc < L::NKC; ++kc) {
+        if constexpr (COMPACT) {
+          if (kc >= nkc) break;   // wavefront-uniform
+        }
         const u32x4 al = *reinterpret_cast<const u32x4 *>(arow_base + astep * kc);
         const u32x2 dk = *reinterpret_cast<const u32x2 *>(&B.y[wave][2 * kc + (q & 1)][8 * lg + (n >> 1)][0]);
         const uint32_t l0 = pk_shl16(dk.x, shl2), h0 = pk_shr16(dk.x, shr2);
@@ -929,12 +969,25 @@ hipError_t launch_decode4(const dqk_cache &c, const float *q_prime, const int32_
     const int n = compute_units();
     if (n > 0 && items > n && items <= 2 * n) ncu = n;
   }
-  if (c.head_dim == 64)
-    hipLaunchKernelGGL((decode4_kernel<64>), grid, block, 0, s, c, q_prime, sel_idx, shared ? 1 : 0, hq, keep, scale2, nsplit,
-                       bps, ncu, ws);
-  else
-    hipLaunchKernelGGL((decode4_kernel<128>), grid, block, 0, s, c, q_prime, sel_idx, shared ? 1 : 0, hq, keep, scale2, nsplit,
-                       bps, ncu, ws);
+  // group-shared kept sets use compact slots: only the K chunks that hold the
+  // keep - 1 kept channels other than 0 are worked on
+  const int nkc = shared ? (keep - 1 + 15) / 16 : c.head_dim / 16;
+  const int sh = shared ? 1 : 0;
+  if (c.head_dim == 64) {
+    if (shared)
+      hipLaunchKernelGGL((decode4_kernel<64, true>), grid, block, 0, s, c, q_prime, sel_idx, sh, hq, keep, scale2,
+                         nsplit, bps, ncu, nkc, ws);
+    else
+      hipLaunchKernelGGL((decode4_kernel<64, false>), grid, block, 0, s, c, q_prime, sel_idx, sh, hq, keep, scale2,
+                         nsplit, bps, ncu, nkc, ws);
+  } else {
+    if (shared)
+      hipLaunchKernelGGL((decode4_kernel<128, true>), grid, block, 0, s, c, q_prime, sel_idx, sh, hq, keep, scale2,
+                         nsplit, bps, ncu, nkc, ws);
+    else
+      hipLaunchKernelGGL((decode4_kernel<128, false>), grid, block, 0, s, c, q_prime, sel_idx, sh, hq, keep, scale2,
+                         nsplit, bps, ncu, nkc, ws);
+  }
   return hipGetLastError();
 }
 

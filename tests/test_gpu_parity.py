@@ -768,11 +768,13 @@ def decode_shared_case(orc, wl, sparsity=40, sm_mult=1.0, splits=(0,)):
         say(f"  split {sp}: max rel err {err:.3e}")
         assert err <= REL_TOL, (sp, err)
         outs.append(out)
-    # the same sets laid out per head through the per-head decode: bitwise equal
+    # the same sets laid out per head through the per-head decode (channel i + 1
+    # in slot i, where the shared decode packs the kept channels into the first
+    # slots: the products are summed in another order) agree to the tolerance
     per = torch.from_numpy(orc.per_head(idx.cpu().numpy(), wl.group)).cuda()
     for sp, out in zip(splits, outs):
         again = M.decode_attention(g, qp, per, sm, split_tokens=sp).cpu().numpy()
-        assert np.array_equal(again.view(np.uint32), out.view(np.uint32)), sp
+        assert rel_err(again, out) <= REL_TOL, sp
     return outs
 
 
