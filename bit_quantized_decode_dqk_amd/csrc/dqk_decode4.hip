@@ -148,29 +148,40 @@ template <int D, bool COMPACT>
 __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
                                                                const float *__restrict__ qp,
                                                                const int32_t *__restrict__ sel,
-                                                               int shared, int hq, int keep, float scale2,
-                                                               int nsplit, int bps, int ncu, int nkc,
-                                                               float *__restrict__ ws) {
+                                                               int shared, int hq, int nsl, int grid3, int keep,
+                                                               float scale2, int nsplit, int bps, int ncu_q,
+                                                               int ncu_r, int nkc, float *__restrict__ ws) {
   using L = Lay4<D>;
   constexpr int G = kG4;
   __shared__ Smem4<D> sm;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: block and tile offsets stay scalar
   // Work item (unit, split s) in split-major order: workgroups of one split index
-  // run together.  A KV head with more than four query heads is served in slices
-  // of four, one workgroup each; the slices of one work item get workgroup ids
-  // eight apart, which go to the same XCD (workgroups are dealt round-robin over
-  // the eight XCDs), so a later slice finds the item's bytes in that XCD's L2.
+  // run together.  With one slice of four query heads per KV head (nsl == 1) the
+  // grid is (KV head, row, split) where it fits (grid3), so that the linear
+  // workgroup id is the item s * units + unit and no division stands between the
+  // start and the length load.  Otherwise the grid is one-dimensional; a KV head
+  // with more than four query heads is then served in nsl slices of four, one
+  // workgroup each, and the slices of one work item get workgroup ids eight apart,
+  // which go to the same XCD (workgroups are dealt round-robin over the eight
+  // XCDs), so a later slice finds the item's bytes in that XCD's L2.
   const int units = c.batch * c.num_kv_heads;
-  const int nsl = hq / (c.num_kv_heads * G);
-  int item = blockIdx.x, slice = 0;
-  if (nsl > 1) {
+  int b, g, s, slice = 0;
+  if (grid3) {
+    g = blockIdx.x;
+    b = blockIdx.y;
+    s = blockIdx.z;
+  } else {
     slice = (blockIdx.x >> 3) % nsl;
-    item = (blockIdx.x / (8 * nsl)) * 8 + (blockIdx.x & 7);
+    const int item = (blockIdx.x / (8 * nsl)) * 8 + (blockIdx.x & 7);
     if (item >= units * nsplit) return;   // the grid is padded to whole groups of eight items
+    const int unit = item % units;
+    s = item / units;
+    b = unit / c.num_kv_heads;
+    g = unit % c.num_kv_heads;
   }
-  const int unit = item % units, s = item / units;
-  const int b = unit / c.num_kv_heads, g = unit % c.num_kv_heads;
+  const int unit = b * c.num_kv_heads + g;
+  const int len = max(0, min(c.lengths[b], c.capacity));
   // The slice's q' rows (all channels) and kept-channel lists are loaded before
   // anything waits, in parallel with the length: one round trip for the setup.
   const size_t row0 = (size_t)b * hq + (size_t)g * G * nsl + (size_t)G * slice;
@@ -181,27 +192,32 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
   for (int k = 0; k < SJ; ++k) {
     const int e = tid + kThreads4 * k;
     qv[k] = qp[row0 * D + e];
-    // the head's kept set: its own row, or its KV head's shared one
-    sv[k] = e < G * keep ? (shared ? sel[(size_t)unit * keep + e % keep] : sel[row0 * keep + e]) : -1;
+    // the head's kept set: its own row, or its KV head's shared one (position
+    // e mod keep, by subtraction: e < G keep)
+    int es = e;
+#pragma unroll
+    for (int h = 1; h < G; ++h) es = es >= keep ? es - keep : es;
+    sv[k] = e < G * keep ? (shared ? sel[(size_t)unit * keep + es] : sel[row0 * keep + e]) : -1;
   }
   // compact slots: the shared kept list without channel 0, one slot per lane
   int uch = -1;
   if constexpr (COMPACT) {
     if (tid < D && tid + 1 < keep) uch = sel[(size_t)unit * keep + tid + 1];
   }
-  const int len = max(0, min(c.lengths[b], c.capacity));
   const int nblk_all = (len + kBlock4 - 1) / kBlock4;
   // bps > 0: split s is blocks [s bps, (s + 1) bps) of the row.  Else the row's
   // blocks are shared out over the nsplit splits: evenly, or, when two workgroups
-  // share each compute unit (ncu > 0: the number of compute units, workgroup ids
-  // below it being the first on their unit), unevenly.  The first workgroup on a
+  // share each compute unit (ncu = ncu_q * units + ncu_r > 0: the number of
+  // compute units, workgroup ids below it being the first on their unit),
+  // unevenly.  The first workgroup on a
   // unit issues ahead of the second (older wavefronts win the issue arbitration)
   // and would finish well before it, so the splits dispatched second take 7/8 of
   // the average share and the first ones the rest, at most one chunk each (with
   // between 4 and about 8 blocks per split on average).
   int blo, bhi;
   {
-    const int fs = ncu > 0 ? min(nsplit, max(0, (ncu - unit + units - 1) / units)) : 0;   // first-slot splits
+    // first-slot splits: items s * units + unit below ncu
+    const int fs = ncu_q + ncu_r > 0 ? min(nsplit, ncu_q + (unit < ncu_r ? 1 : 0)) : 0;
     const int ss = nsplit - fs;
     if (bps > 0) {
       blo = min(s * bps, nblk_all);
@@ -212,17 +228,22 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
       // first-slot splits share the rest evenly, at most one chunk each.  The last
       // split, which also works out the exact logits of an unfinished last key
       // group, takes one block less when there is one.
+      // (32-bit arithmetic: here nblk_all <= 10 nsplit and nsplit <= 2 ncu, with
+      // ncu below 4096, so that every product stays below 2^31)
       const int cut = len % kGroup != 0 ? 1 : 0;
-      const long long wt = 9LL * fs + 7LL * ss;
-      const int a2 = max((int)((7LL * nblk_all) / wt), (nblk_all + cut - kChunk4 * fs + ss - 1) / ss);
+      const uint32_t wt = 9u * fs + 7u * ss;
+      const int a2 = max((int)((7u * (uint32_t)nblk_all) / wt), (nblk_all + cut - kChunk4 * fs + ss - 1) / ss);
       const int t1 = nblk_all - a2 * ss + cut;
       if (s < fs) {
-        blo = (int)(((long long)t1 * s) / fs);
-        bhi = (int)(((long long)t1 * (s + 1)) / fs);
+        blo = (int)(((uint32_t)t1 * (uint32_t)s) / (uint32_t)fs);
+        bhi = (int)(((uint32_t)t1 * (uint32_t)(s + 1)) / (uint32_t)fs);
       } else {
         blo = t1 + a2 * (s - fs);
         bhi = s == nsplit - 1 ? nblk_all : blo + a2;
       }
+    } else if ((unsigned long long)nblk_all * (unsigned long long)nsplit < (1ull << 32)) {
+      blo = (int)(((uint32_t)s * (uint32_t)nblk_all) / (uint32_t)nsplit);
+      bhi = (int)(((uint32_t)(s + 1) * (uint32_t)nblk_all) / (uint32_t)nsplit);
     } else {
       blo = (int)(((long long)s * nblk_all) / nsplit);
       bhi = (int)(((long long)(s + 1) * nblk_all) / nsplit);
@@ -908,20 +929,29 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
       }
   }
   __syncthreads();
-  for (int e = tid; e < G * D; e += kThreads4) {
-    const int h = e / D, ch = e % D;
+  // Straight-line: every LDS read of an element is issued before any is used, and
+  // a wavefront without tokens is dropped by selects, not branches.
+  static_assert((G * D) % kThreads4 == 0, "whole rounds of elements");
+#pragma unroll
+  for (int k = 0; k < (G * D) / kThreads4; ++k) {
+    const int e = tid + kThreads4 * k, h = e / D, ch = e % D;
+    float lw[kWaves4], mw[kWaves4], ow[kWaves4];
+#pragma unroll
+    for (int w = 0; w < kWaves4; ++w) {
+      lw[w] = sm.w[w].lstate[h];
+      mw[w] = sm.w[w].mstate[h];
+      ow[w] = sm.w[w].u.merge[h][ch];
+    }
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves4; ++w)
-      if (sm.w[w].lstate[h] > 0.0f) M = fmaxf(M, sm.w[w].mstate[h]);
+    for (int w = 0; w < kWaves4; ++w) M = lw[w] > 0.0f ? fmaxf(M, mw[w]) : M;
     float o = 0.0f, Lsum = 0.0f;
 #pragma unroll
     for (int w = 0; w < kWaves4; ++w) {
-      if (sm.w[w].lstate[h] > 0.0f) {
-        const float f = exp2f(sm.w[w].mstate[h] - M);
-        o = fmaf(sm.w[w].u.merge[h][ch], f, o);
-        Lsum = fmaf(sm.w[w].lstate[h], f, Lsum);
-      }
+      const bool live = lw[w] > 0.0f;
+      const float f = exp2f((live ? mw[w] : M) - M);
+      o = live ? fmaf(ow[w], f, o) : o;
+      Lsum = live ? fmaf(lw[w], f, Lsum) : Lsum;
     }
     wsp[h * (D + kPartialHead) + kPartialHead + ch] = o;
     if (ch == 0) {
@@ -959,34 +989,43 @@ hipError_t launch_decode4(const dqk_cache &c, const float *q_prime, const int32_
   // otherwise (and always for the library's own split count) each split takes an
   // equal share of its row's current blocks
   const int bps = !even && split % kBlock4 == 0 ? split / kBlock4 : 0;
-  const int items = c.batch * c.num_kv_heads * nsplit;
+  const int units = c.batch * c.num_kv_heads;
+  const int items = units * nsplit;
   const int nsl = hq / (c.num_kv_heads * kG4);
-  const dim3 grid((unsigned)(nsl > 1 ? (items + 7) / 8 * 8 * nsl : items)), block(kThreads4);
+  // one slice per KV head: (KV head, row, split), whose linear order is the item
+  // order, if rows and splits fit the grid's second and third dimensions; else
+  // the padded one-dimensional grid (of the slices)
+  const int grid3 = nsl == 1 && c.batch <= 65535 && nsplit <= 65535 ? 1 : 0;
+  const dim3 grid = grid3 ? dim3((unsigned)c.num_kv_heads, (unsigned)c.batch, (unsigned)nsplit)
+                          : dim3((unsigned)((items + 7) / 8 * 8 * nsl));
+  const dim3 block(kThreads4);
   // uneven shares for two workgroups per compute unit (the library's own split of
-  // groups of four only)
+  // groups of four only; the kernel's share arithmetic is 32-bit for fewer than
+  // 4096 compute units)
   int ncu = 0;
   if (even && nsl == 1 && bps == 0) {
     const int n = compute_units();
-    if (n > 0 && items > n && items <= 2 * n) ncu = n;
+    if (n > 0 && n < 4096 && items > n && items <= 2 * n) ncu = n;
   }
+  const int ncu_q = ncu / units, ncu_r = ncu % units;
   // group-shared kept sets use compact slots: only the K chunks that hold the
   // keep - 1 kept channels other than 0 are worked on
   const int nkc = shared ? (keep - 1 + 15) / 16 : c.head_dim / 16;
   const int sh = shared ? 1 : 0;
   if (c.head_dim == 64) {
     if (shared)
-      hipLaunchKernelGGL((decode4_kernel<64, true>), grid, block, 0, s, c, q_prime, sel_idx, sh, hq, keep, scale2,
-                         nsplit, bps, ncu, nkc, ws);
+      hipLaunchKernelGGL((decode4_kernel<64, true>), grid, block, 0, s, c, q_prime, sel_idx, sh, hq, nsl, grid3, keep,
+                         scale2, nsplit, bps, ncu_q, ncu_r, nkc, ws);
     else
-      hipLaunchKernelGGL((decode4_kernel<64, false>), grid, block, 0, s, c, q_prime, sel_idx, sh, hq, keep, scale2,
-                         nsplit, bps, ncu, nkc, ws);
+      hipLaunchKernelGGL((decode4_kernel<64, false>), grid, block, 0, s, c, q_prime, sel_idx, sh, hq, nsl, grid3, keep,
+                         scale2, nsplit, bps, ncu_q, ncu_r, nkc, ws);
   } else {
     if (shared)
-      hipLaunchKernelGGL((decode4_kernel<128, true>), grid, block, 0, s, c, q_prime, sel_idx, sh, hq, keep, scale2,
-                         nsplit, bps, ncu, nkc, ws);
+      hipLaunchKernelGGL((decode4_kernel<128, true>), grid, block, 0, s, c, q_prime, sel_idx, sh, hq, nsl, grid3, keep,
+                         scale2, nsplit, bps, ncu_q, ncu_r, nkc, ws);
     else
-      hipLaunchKernelGGL((decode4_kernel<128, false>), grid, block, 0, s, c, q_prime, sel_idx, sh, hq, keep, scale2,
-                         nsplit, bps, ncu, nkc, ws);
+      hipLaunchKernelGGL((decode4_kernel<128, false>), grid, block, 0, s, c, q_prime, sel_idx, sh, hq, nsl, grid3, keep,
+                         scale2, nsplit, bps, ncu_q, ncu_r, nkc, ws);
   }
   return hipGetLastError();
 }
