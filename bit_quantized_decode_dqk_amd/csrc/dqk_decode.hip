@@ -101,7 +101,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(dqk_cache c,
                                                              const int32_t *__restrict__ sel,
                                                              int shared, int hq, int keep, float scale2,
                                                              int split, int nsplit,
-                                                             float *__restrict__ ws) {
+                                                             float *__restrict__ ws,
+                                                             float *__restrict__ out) {
   using K = Cfg<D, G>;
   __shared__ Smem<D, G> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -115,9 +116,16 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(dqk_cache c,
   const int t_begin = s * split;
   const int t_end = min(t_begin + split, len);
   float *wsp = ws + (size_t)item * G * (D + kPartialHead);
+  // out != nullptr: a single split per row, whose normalized output is written
+  // directly (what the combine makes of one partial); an empty row gives zeros
+  float *outp = out ? out + ((size_t)b * hq + (size_t)g * G) * D : nullptr;
   if (t_begin >= t_end) {
-    for (int e = tid; e < G * (D + kPartialHead); e += kThreads)
-      wsp[e] = (e % (D + kPartialHead) == 0) ? -INFINITY : 0.0f;
+    if (outp) {
+      for (int e = tid; e < G * D; e += kThreads) outp[e] = 0.0f;
+    } else {
+      for (int e = tid; e < G * (D + kPartialHead); e += kThreads)
+        wsp[e] = (e % (D + kPartialHead) == 0) ? -INFINITY : 0.0f;
+    }
     return;
   }
 
@@ -542,25 +550,37 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(dqk_cache c,
       }
   }
   __syncthreads();
+  // Straight-line: every LDS read of an element is issued before any is used, and
+  // a wavefront without tokens is dropped by selects, not branches.
   for (int e = tid; e < G * D; e += kThreads) {
     const int h = e / D, ch = e % D;
+    float lw[kWaves], mw[kWaves], ow[kWaves];
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      lw[w] = sm.w[w].lstate[h];
+      mw[w] = sm.w[w].mstate[h];
+      ow[w] = sm.w[w].u.merge[h][ch];
+    }
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w)
-      if (sm.w[w].lstate[h] > 0.0f) M = fmaxf(M, sm.w[w].mstate[h]);
+    for (int w = 0; w < kWaves; ++w) M = lw[w] > 0.0f ? fmaxf(M, mw[w]) : M;
     float o = 0.0f, L = 0.0f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      if (sm.w[w].lstate[h] > 0.0f) {
-        const float f = exp2f(sm.w[w].mstate[h] - M);
-        o = fmaf(sm.w[w].u.merge[h][ch], f, o);
-        L = fmaf(sm.w[w].lstate[h], f, L);
-      }
+      const bool live = lw[w] > 0.0f;
+      const float f = exp2f((live ? mw[w] : M) - M);
+      o = live ? fmaf(ow[w], f, o) : o;
+      L = live ? fmaf(lw[w], f, L) : L;
     }
-    wsp[h * (D + kPartialHead) + kPartialHead + ch] = o;
-    if (ch == 0) {
-      wsp[h * (D + kPartialHead) + 0] = M;
-      wsp[h * (D + kPartialHead) + 1] = L;
+    if (outp) {
+      const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+      outp[h * D + ch] = o * inv;
+    } else {
+      wsp[h * (D + kPartialHead) + kPartialHead + ch] = o;
+      if (ch == 0) {
+        wsp[h * (D + kPartialHead) + 0] = M;
+        wsp[h * (D + kPartialHead) + 1] = L;
+      }
     }
   }
 }
@@ -571,10 +591,11 @@ hipError_t launch_decode_t(const dqk_cache &c, const float *qp, const int32_t *s
                            hipStream_t s) {
   const int nsplit = num_splits(c.capacity, split);
   const int items = c.batch * c.num_kv_heads * nsplit;
+  // one split per row: the kernel writes the output itself and no combine runs
   hipLaunchKernelGGL((decode_kernel<D, G>), dim3((unsigned)items), dim3(kThreads), 0, s, c, qp,
-                     sel, shared, hq, keep, scale2, split, nsplit, ws);
+                     sel, shared, hq, keep, scale2, split, nsplit, ws, nsplit == 1 ? out : nullptr);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || nsplit == 1) return e;
   return launch_combine(ws, c.batch, hq, c.num_kv_heads, D, nsplit, out, s);
 }
 
@@ -591,9 +612,12 @@ hipError_t launch_decode_d(const dqk_cache &c, const float *qp, const int32_t *s
         return hq == 4 * c.num_kv_heads
                    ? launch_decode_t<D, 4>(c, qp, sel, shared, hq, keep, scale2, split, out, ws, s)
                    : launch_decode_t<D, 8>(c, qp, sel, shared, hq, keep, scale2, split, out, ws, s);
-      const hipError_t e = launch_decode4(c, qp, sel, shared != 0, hq, keep, scale2, split, even, ws, s);
-      if (e != hipSuccess) return e;
-      return launch_combine(ws, c.batch, hq, c.num_kv_heads, D, num_splits(c.capacity, split), out, s);
+      const int nsplit = num_splits(c.capacity, split);
+      // one split per row: the kernel writes the output itself and no combine runs
+      const hipError_t e =
+          launch_decode4(c, qp, sel, shared != 0, hq, keep, scale2, split, even, ws, nsplit == 1 ? out : nullptr, s);
+      if (e != hipSuccess || nsplit == 1) return e;
+      return launch_combine(ws, c.batch, hq, c.num_kv_heads, D, nsplit, out, s);
     }
     default: return hipErrorInvalidValue;
   }

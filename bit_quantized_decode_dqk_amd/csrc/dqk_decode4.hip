@@ -150,7 +150,8 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
                                                                const int32_t *__restrict__ sel,
                                                                int shared, int hq, int nsl, int grid3, int keep,
                                                                float scale2, int nsplit, int bps, int ncu_q,
-                                                               int ncu_r, int nkc, float *__restrict__ ws) {
+                                                               int ncu_r, int nkc, float *__restrict__ ws,
+                                                               float *__restrict__ out) {
   using L = Lay4<D>;
   constexpr int G = kG4;
   __shared__ Smem4<D> sm;
@@ -253,9 +254,16 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
   const int t_end = min(bhi * kBlock4, len);
   const int nb = bhi - blo;
   float *wsp = ws + (((size_t)unit * nsplit + s) * nsl + slice) * G * (D + kPartialHead);
+  // out != nullptr: a single split per row, whose normalized output is written
+  // directly (what the combine makes of one partial); an empty row gives zeros
+  float *outp = out ? out + row0 * D : nullptr;
   if (t_begin >= t_end) {
-    for (int e = tid; e < G * (D + kPartialHead); e += kThreads4)
-      wsp[e] = (e % (D + kPartialHead) == 0) ? -INFINITY : 0.0f;
+    if (outp) {
+      for (int e = tid; e < G * D; e += kThreads4) outp[e] = 0.0f;
+    } else {
+      for (int e = tid; e < G * (D + kPartialHead); e += kThreads4)
+        wsp[e] = (e % (D + kPartialHead) == 0) ? -INFINITY : 0.0f;
+    }
     return;
   }
 
@@ -953,10 +961,15 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
       o = live ? fmaf(ow[w], f, o) : o;
       Lsum = live ? fmaf(lw[w], f, Lsum) : Lsum;
     }
-    wsp[h * (D + kPartialHead) + kPartialHead + ch] = o;
-    if (ch == 0) {
-      wsp[h * (D + kPartialHead) + 0] = M;
-      wsp[h * (D + kPartialHead) + 1] = Lsum;
+    if (outp) {
+      const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
+      outp[h * D + ch] = o * inv;
+    } else {
+      wsp[h * (D + kPartialHead) + kPartialHead + ch] = o;
+      if (ch == 0) {
+        wsp[h * (D + kPartialHead) + 0] = M;
+        wsp[h * (D + kPartialHead) + 1] = Lsum;
+      }
     }
   }
 }
@@ -983,7 +996,7 @@ bool decode4_supported(const dqk_cache &c, int hq) {
 
 hipError_t launch_decode4(const dqk_cache &c, const float *q_prime, const int32_t *sel_idx,
                           bool shared, int hq, int keep, float scale2, int split, bool even,
-                          float *ws, hipStream_t s) {
+                          float *ws, float *out, hipStream_t s) {
   const int nsplit = num_splits(c.capacity, split);
   // a caller's split of whole blocks covers exactly its split tokens of every row;
   // otherwise (and always for the library's own split count) each split takes an
@@ -1015,17 +1028,17 @@ hipError_t launch_decode4(const dqk_cache &c, const float *q_prime, const int32_
   if (c.head_dim == 64) {
     if (shared)
       hipLaunchKernelGGL((decode4_kernel<64, true>), grid, block, 0, s, c, q_prime, sel_idx, sh, hq, nsl, grid3, keep,
-                         scale2, nsplit, bps, ncu_q, ncu_r, nkc, ws);
+                         scale2, nsplit, bps, ncu_q, ncu_r, nkc, ws, out);
     else
       hipLaunchKernelGGL((decode4_kernel<64, false>), grid, block, 0, s, c, q_prime, sel_idx, sh, hq, nsl, grid3, keep,
-                         scale2, nsplit, bps, ncu_q, ncu_r, nkc, ws);
+                         scale2, nsplit, bps, ncu_q, ncu_r, nkc, ws, out);
   } else {
     if (shared)
       hipLaunchKernelGGL((decode4_kernel<128, true>), grid, block, 0, s, c, q_prime, sel_idx, sh, hq, nsl, grid3, keep,
-                         scale2, nsplit, bps, ncu_q, ncu_r, nkc, ws);
+                         scale2, nsplit, bps, ncu_q, ncu_r, nkc, ws, out);
     else
       hipLaunchKernelGGL((decode4_kernel<128, false>), grid, block, 0, s, c, q_prime, sel_idx, sh, hq, nsl, grid3, keep,
-                         scale2, nsplit, bps, ncu_q, ncu_r, nkc, ws);
+                         scale2, nsplit, bps, ncu_q, ncu_r, nkc, ws, out);
   }
   return hipGetLastError();
 }

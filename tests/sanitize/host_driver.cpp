@@ -34,7 +34,7 @@ hipError_t launch_append_select(const dqk_cache &, const void *, const void *, b
 hipError_t launch_decode(const dqk_cache &, const float *, const int32_t *, bool, int, int, float,
                          int, bool, float *, float *, hipStream_t) { STUB }
 hipError_t launch_decode4(const dqk_cache &, const float *, const int32_t *, bool, int, int, float,
-                          int, bool, float *, hipStream_t) { STUB }
+                          int, bool, float *, float *, hipStream_t) { STUB }
 hipError_t launch_dequant(const dqk_cache &, float *, float *, hipStream_t) { STUB }
 hipError_t launch_cache_grow(const dqk_cache &, const dqk_cache &, hipStream_t) { STUB }
 hipError_t launch_bf16_decode(const uint16_t *, const uint16_t *, const uint16_t *, const int32_t *,
