@@ -24,7 +24,7 @@ namespace appb {
 constexpr int kThreads = 256;
 
 template <int D>
-struct AppendSmem {
+struct __attribute__((aligned(16))) AppendSmem {
   float kx[kGroup][D];   // new keys of the group (fp32)
   float kp[kGroup][D];   // transformed keys
   float vx[kGroup][D];   // new values (fp32)
@@ -38,9 +38,12 @@ __device__ __forceinline__ float load_in(const void *p, size_t i) {
 }
 
 // bcol: this thread's column j = tid % D of B_g, all D rows, loaded at kernel
-// start before anything waits (used by single-token appends; bulk appends
-// stream the rows of B from bmat).
-template <int D, bool BF16>
+// start before anything waits (used by appends of at most one token per thread
+// slot).  Otherwise the rows of B are streamed from bmat: one output channel per
+// thread, or in BULK workgroups 4 channels x 4 tokens per thread (16-byte loads
+// of B rows and of the inputs in LDS).  Every form runs the same FMA chain per
+// output in the same order, so they agree bit for bit.
+template <int D, bool BF16, bool BULK>
 __device__ __forceinline__ void store_group(const dqk_cache &c, int b, int g, int grp, int L, int n,
                                             const void *k_new, const void *v_new,
                                             const float (&bcol)[D], const float *__restrict__ bmat,
@@ -75,8 +78,47 @@ __device__ __forceinline__ void store_group(const dqk_cache &c, int b, int g, in
   }
   __syncthreads();
 
-  // k' = k B: thread owns output channel j for tokens r0, r0+S, ...
-  {
+  // k' = k B, each output one FMA chain over the input channels in ascending order
+  if constexpr (BULK) {
+    // 4 output channels x TPT tokens per thread: per step of 4 input channels, 4 rows
+    // of B (16-byte loads; the next step's in flight) and TPT 16-byte LDS reads of the
+    // tokens' inputs feed 16 TPT FMAs.  bmat is 16-byte aligned for this form.
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    constexpr int CG = D / 4, TG = kThreads / CG, TPT = kGroup / TG;
+    const int cj = 4 * (tid % CG), tr = TPT * (tid / CG);
+    const f4 *brow = reinterpret_cast<const f4 *>(bmat + (size_t)g * D * D + cj);   // row i: brow[i * D / 4]
+    float acc[TPT][4];
+#pragma unroll
+    for (int rr = 0; rr < TPT; ++rr)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) acc[rr][jj] = 0.0f;
+    f4 bq[4], bn[4];
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) bq[ii] = brow[(size_t)ii * (D / 4)];
+#pragma unroll 2
+    for (int i0 = 0; i0 < D; i0 += 4) {
+      const int i1 = i0 + 4 < D ? i0 + 4 : i0;   // the last step re-reads its own rows
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) bn[ii] = brow[(size_t)(i1 + ii) * (D / 4)];
+      f4 kq[TPT];
+#pragma unroll
+      for (int rr = 0; rr < TPT; ++rr) kq[rr] = *reinterpret_cast<const f4 *>(&sm.kx[tr + rr][i0]);
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+        for (int rr = 0; rr < TPT; ++rr)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) acc[rr][jj] = __builtin_fmaf(kq[rr][ii], bq[ii][jj], acc[rr][jj]);
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) bq[ii] = bn[ii];
+    }
+#pragma unroll
+    for (int rr = 0; rr < TPT; ++rr)
+      if (tr + rr < cnt) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) sm.kp[tr + rr][cj + jj] = acc[rr][jj];
+      }
+  } else {
     constexpr int S = kThreads / D;           // token slots per channel
     constexpr int R = kGroup / S;             // tokens per thread at most
     const int j = tid % D, r0 = tid / D;
@@ -86,22 +128,28 @@ __device__ __forceinline__ void store_group(const dqk_cache &c, int b, int g, in
       for (int i = 0; i < D; ++i) acc = __builtin_fmaf(sm.kx[r0][i], bcol[i], acc);
       if (r0 < cnt) sm.kp[r0][j] = acc;
     } else {
-      // rows of B fetched kBRows at a time so that many loads are in flight
+      // rows of B fetched kBRows at a time, the next batch in flight while the
+      // current one is used (the FMA order per output is unchanged)
       constexpr int kBRows = 16;
       const float *bc = bmat + (size_t)g * D * D + j;
       float acc[R];
 #pragma unroll
       for (int m = 0; m < R; ++m) acc[m] = 0.0f;
+      float bv[kBRows], bn[kBRows];
+#pragma unroll
+      for (int r = 0; r < kBRows; ++r) bv[r] = bc[(size_t)r * D];
 #pragma unroll 1
       for (int i0 = 0; i0 < D; i0 += kBRows) {   // (a full unroll would spill)
-        float bv[kBRows];
+        const int i1 = i0 + kBRows < D ? i0 + kBRows : i0;   // the last batch re-reads itself
 #pragma unroll
-        for (int r = 0; r < kBRows; ++r) bv[r] = bc[(size_t)(i0 + r) * D];
+        for (int r = 0; r < kBRows; ++r) bn[r] = bc[(size_t)(i1 + r) * D];
 #pragma unroll
         for (int r = 0; r < kBRows; ++r)
 #pragma unroll
           for (int m = 0; m < R; ++m)
             acc[m] = __builtin_fmaf(sm.kx[r0 + m * S][i0 + r], bv[r], acc[m]);
+#pragma unroll
+        for (int r = 0; r < kBRows; ++r) bv[r] = bn[r];
       }
 #pragma unroll
       for (int m = 0; m < R; ++m)
@@ -169,7 +217,9 @@ __device__ __forceinline__ void store_group(const dqk_cache &c, int b, int g, in
   __syncthreads();
 }
 
-template <int D, bool BF16>
+// BULK: appends of many tokens per row (prefill), which never use a held column of
+// B; such workgroups load none, and hold no registers for one.
+template <int D, bool BF16, bool BULK = false>
 __device__ __forceinline__ void append_block(int block, const dqk_cache &c, const void *k_new,
                                              const void *v_new, const float *__restrict__ bmat,
                                              const int32_t *__restrict__ n_new, int max_new,
@@ -183,13 +233,15 @@ __device__ __forceinline__ void append_block(int block, const dqk_cache &c, cons
   // max_new of them); the others load nothing, which halves the workgroup's
   // reads of B_g for one-token appends.
   float bcol[D];
-  if ((int)(threadIdx.x / D) < max_new) {
-    const float *bp = bmat + (size_t)g * D * D + threadIdx.x % D;
+  if constexpr (!BULK) {
+    if ((int)(threadIdx.x / D) < max_new) {
+      const float *bp = bmat + (size_t)g * D * D + threadIdx.x % D;
 #pragma unroll
-    for (int i = 0; i < D; ++i) bcol[i] = bp[(size_t)i * D];
-  } else {
+      for (int i = 0; i < D; ++i) bcol[i] = bp[(size_t)i * D];
+    } else {
 #pragma unroll
-    for (int i = 0; i < D; ++i) bcol[i] = 0.0f;
+      for (int i = 0; i < D; ++i) bcol[i] = 0.0f;
+    }
   }
   const int L = c.lengths[b];
   const int n = max(0, min(min(n_new[b], max_new), c.capacity - L));
@@ -200,8 +252,9 @@ __device__ __forceinline__ void append_block(int block, const dqk_cache &c, cons
   const bool merged = g1 > g0 && (L % kGroup) != 0 && ((L + n) % kGroup) != 0;
   const int ngroups = g1 - g0 + 1;
   if (bi < ngroups && !(merged && bi == ngroups - 1)) {
-    store_group<D, BF16>(c, b, g, g0 + bi, L, n, k_new, v_new, bcol, bmat, max_new, sm);
-    if (merged && bi == 0) store_group<D, BF16>(c, b, g, g1, L, n, k_new, v_new, bcol, bmat, max_new, sm);
+    store_group<D, BF16, BULK>(c, b, g, g0 + bi, L, n, k_new, v_new, bcol, bmat, max_new, sm);
+    if (merged && bi == 0)
+      store_group<D, BF16, BULK>(c, b, g, g1, L, n, k_new, v_new, bcol, bmat, max_new, sm);
   }
   // Length commit: every workgroup of the row (with or without a group to store)
   // counts itself in on the row's arrival counter once all of its wavefronts
