@@ -51,12 +51,10 @@ inline DecodeSplit matrix_decode_split(int capacity, int workgroups) {
   return {balanced_decode_split(capacity, workgroups), true};
 }
 
-// Default split of the general decode: about two workgroups per CU of 256-token
-// splits or more, except that a capacity of at most 1024 tokens is one split, which
-// the decode normalizes itself with no combine launch (at 1024 tokens, 18.3 us per
-// decode call against 20.5 us for four splits and the combine).
+// Default split of the general decode: about two workgroups per CU, splits of 256
+// tokens or more.  (One split of a 1024-token row, which needs no combine launch,
+// measured slower in a replayed step: 18.6 against 12.9 us for select + decode.)
 inline int default_decode_split(int capacity, int units) {
-  if (capacity <= 1024) return capacity;
   const long long slots = 2 * 256LL;
   const long long per = ((long long)capacity * units) / slots;
   const int s = (int)(per / 256 * 256);

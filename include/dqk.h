@@ -166,8 +166,7 @@ dqk_status dqk_decode_workspace_bytes(const dqk_cache *cache, int32_t hq,
  * values share each row's current 256-token blocks out over the splits.  Otherwise
  * split s covers tokens [s split_tokens, (s + 1) split_tokens).  The result does not
  * depend on the split beyond fp32 rounding.  With a single split (split_tokens >=
- * capacity, or the library's choice for a capacity of at most 1024 tokens) the
- * decode writes out itself and the workspace is not touched.
+ * capacity) the decode writes out itself and the workspace is not touched.
  * q_prime: [batch][hq][d] fp32; sel_idx: [batch][hq][keep] as produced by
  * dqk_select_channels; out: [batch][hq][d] fp32; workspace: device scratch of at
  * least dqk_decode_workspace_bytes (contents need no initialization). */

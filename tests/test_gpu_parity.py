@@ -101,6 +101,24 @@ def test_append_gqa_ragged(orc, chunks):
     assert_same_cache(planes_np(g), ref)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_append_bulk_with_unaligned_transform(orc, d):
+    """A bulk append whose B is not 16-byte aligned (one float into a buffer) takes
+    the per-channel streaming form instead of the blocked one: the same planes."""
+    wl = W.custom(f"unaligned-b{d}", 26, 2, 8, 2, d, [300, 77], 320, "bf16", log_uniform_key_scales=True)
+    a, b = W.transforms(wl)
+    k, v = W.prefill_kv(wl)
+    buf = torch.zeros(b.size + 1, dtype=torch.float32, device="cuda")
+    buf[1:] = dev_f32(b).reshape(-1)
+    b_off = buf[1:].view(b.shape)   # 4 bytes past a 16-byte boundary
+    assert b_off.data_ptr() % 16 == 4
+    g = M.Cache(wl.batch, wl.hkv, wl.d, wl.cap)
+    n = max(wl.ctx)
+    M.transform_quantize_append(g, dev_input(k[:, :, :n], wl.dtype), dev_input(v[:, :, :n], wl.dtype),
+                                b_off, dev_i32(list(wl.ctx)))
+    assert_same_cache(planes_np(g), build_oracle(orc, wl, k, v, b))
+
+
 def test_append_head_dim_64_and_capacity_clamp(orc):
     wl = W.custom("d64", 22, 2, 4, 2, 64, [96, 64], 96, "f32", random_outlier_channels=3)
     g, a, b, k, v = build_gpu(wl)
