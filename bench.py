@@ -539,7 +539,9 @@ def transform_fit_report(M, torch, d: int = 128, n_keys: int = 8192, n_q: int = 
                "identity": (np.eye(d, dtype=np.float32), np.eye(d, dtype=np.float32))}
     out = {"keep": keep, "keys": n_keys, "queries": n_q,
            "what": ("share of |q'|^2 kept; relative Frobenius error of pruned logits (exact k', "
-                    "stored INT2 k') and of attention outputs, against exact q.k attention")}
+                    "stored INT2 k') and of attention outputs, against exact q.k attention; "
+                    "relative MSE of the stored INT2 keys in the transformed space and mapped "
+                    "back to the original one")}
     for name, (a, b) in methods.items():
         cache = M.Cache(1, 1, d, n_keys)
         kd = torch.from_numpy(keys).cuda().view(1, 1, n_keys, d)
@@ -560,9 +562,18 @@ def transform_fit_report(M, torch, d: int = 128, n_keys: int = 8192, n_q: int = 
         e_kept = float(np.mean((qm ** 2).sum(1) / (qp ** 2).sum(1)))
         rel = lambda z: float(np.linalg.norm(z - z_ex) / np.linalg.norm(z_ex))
         o = attend(z_int2[:nq_att], vq[0, 0].double().cpu().numpy())
+        # INT2 key error: in the transformed space, and mapped back (k = k' A^T, since
+        # A B^T = I), where the methods share one space
+        kt = kq[0, 0].double().cpu().numpy()
+        mse_t = float(((kt - kexact) ** 2).sum() / (kexact ** 2).sum())
+        kback = kt @ a.astype(np.float64).T
+        k64 = keys.astype(np.float64)
+        mse_o = float(((kback - k64) ** 2).sum() / (k64 ** 2).sum())
         out[name] = {"energy_kept": round(e_kept, 4), "logit_err_pruned": round(rel(z_prune), 4),
                      "logit_err_pruned_int2": round(rel(z_int2), 4),
-                     "attn_out_err_int2_pruned": round(float(np.linalg.norm(o - o_ex) / np.linalg.norm(o_ex)), 4)}
+                     "attn_out_err_int2_pruned": round(float(np.linalg.norm(o - o_ex) / np.linalg.norm(o_ex)), 4),
+                     "int2_key_rel_mse_transformed": round(mse_t, 4),
+                     "int2_key_rel_mse_original": round(mse_o, 4)}
         del cache
     return out
 
