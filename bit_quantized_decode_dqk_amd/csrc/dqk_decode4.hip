@@ -8,10 +8,13 @@
 // workgroup serves the four query heads of one KV head over a share of the
 // sequence's 256-token blocks; only the union U of the group's kept key channels
 // is read (their 2-bit rows are channel-major, so a dropped channel costs no
-// bytes; the workgroup's first block, issued before U is known, reads every
-// channel), together with channel 0's fp16 row and, for the unfinished last
-// group, the exact tail.  Each head's logit uses only its own channels (its
-// coefficient is zero on the others).  Values are never pruned.
+// bytes; with per-head kept sets the workgroup's first block, issued before U is
+// known, reads every channel, while a group-shared set is read first and packed
+// into the first slots), together with channel 0's fp16 row and, for the
+// unfinished last group, the exact tail.  Each head's logit uses only its own
+// channels (its coefficient is zero on the others).  Values are never pruned.
+// The workgroup leaves its partial (m, l, o) per head for the combine, or, when
+// a row has a single split, the normalized output itself.
 //
 // Two passes per chunk of up to ten blocks (2560 tokens):
 //  1. keys.  Every lane of the workgroup issues the same fixed set of buffer
