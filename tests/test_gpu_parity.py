@@ -302,6 +302,72 @@ def test_decode4_many_splits_one_dimensional_grid(orc):
     decode_case(orc, wl, splits=(32, 0, 4096))
 
 
+def _random_cases(n: int, seed: int):
+    """Seeded random shapes for the sweep below: head dimension, group size,
+    capacity (a multiple of 64 or only of 32), ragged lengths with empty rows,
+    keep, split and input type."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        d = int(rng.choice([64, 128]))
+        g = int(rng.choice([1, 2, 4, 8]))
+        hkv = int(rng.integers(1, 4))
+        batch = int(rng.integers(1, 4))
+        cap = int(rng.integers(2, 60)) * (64 if rng.random() < 0.6 else 32)
+        lens = [int(x) for x in rng.integers(0, cap + 1, size=batch)]
+        if rng.random() < 0.3:
+            lens[int(rng.integers(0, batch))] = 0
+        keep = int(rng.integers(1, d + 1))
+        split = int(rng.choice([0, 0, 32 * int(rng.integers(1, 40)), 256 * int(rng.integers(1, 8))]))
+        dtype = "bf16" if rng.random() < 0.7 else "f32"
+        out.append((i, d, g, hkv, batch, cap, lens, keep, split, dtype))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_cases(24, 2024), ids=lambda c: f"r{c[0]}")
+def test_decode_random_shapes(orc, case):
+    """A seeded sweep of random shapes through append, select and decode against the
+    oracle: planes bit-exact, q' and kept sets bit-exact, outputs within 2e-3 (an
+    empty row gives zeros); the no-allocation decode bitwise equal to the workspace
+    one; the group-shared selection and decode against the oracle's."""
+    i, d, g, hkv, batch, cap, lens, keep, split, dtype = case
+    wl = W.custom(f"rand{i}", 70 + i, batch, g * hkv, hkv, d, lens, cap, dtype,
+                  log_uniform_key_scales=(dtype == "bf16"), student_t_queries=(g == 8))
+    say("random", i, "d", d, "G", g, "hkv", hkv, "batch", batch, "cap", cap, "lens", lens,
+        "keep", keep, "split", split, dtype)
+    gc, a, b, k, v = build_gpu(wl)
+    ref = build_oracle(orc, wl, k, v, b)
+    assert_same_cache(planes_np(gc), ref)
+    q = W.queries(wl)
+    qp, idx = gpu_queries(wl, q, a, keep)
+    qpo, idxo = orc.queries(q, a, wl.hkv, keep)
+    assert np.array_equal(qp.cpu().numpy().view(np.uint32), qpo.view(np.uint32))
+    assert np.array_equal(idx.cpu().numpy(), idxo)
+    sm = W.default_sm_scale(d)
+    o_ref = ref.decode(qpo, idxo, sm)
+    out = M.decode_attention(gc, qp, idx, sm, split_tokens=split).cpu().numpy()
+    err = rel_err(out, o_ref)
+    say(f"  max rel err {err:.3e}")
+    assert err <= REL_TOL, err
+    for bb, n in enumerate(lens):
+        if n == 0:
+            assert not out[bb].any()
+    # the entry point that allocates nothing: the same kernels and splits, bitwise
+    if M.decode_workspace_bytes(gc, wl.hq, split) <= M.DECODE_SCRATCH_BYTES:
+        na = M.decode_attention_noalloc(gc, qp, idx, sm, split_tokens=split).cpu().numpy()
+        assert np.array_equal(na.view(np.uint32), out.view(np.uint32))
+    # group-shared kept sets on the same cache
+    qps, idxs = M.select_channels_shared(dev_input(q, wl.dtype), dev_f32(a), wl.hkv, keep)
+    qpso, idxso = orc.queries_shared(q, a, wl.hkv, keep)
+    assert np.array_equal(qps.cpu().numpy().view(np.uint32), qpso.view(np.uint32))
+    assert np.array_equal(idxs.cpu().numpy(), idxso)
+    o_sh = ref.decode(qpso, orc.per_head(idxso, wl.group), sm)
+    sh = M.decode_attention_shared(gc, qps, idxs, sm, split_tokens=split).cpu().numpy()
+    err = rel_err(sh, o_sh)
+    say(f"  shared: max rel err {err:.3e}")
+    assert err <= REL_TOL, err
+
+
 @pytest.mark.parametrize("hq,hkv,d,cap", [(1, 1, 64, 1344), (2, 1, 64, 1344), (8, 1, 64, 1344),
                                           (4, 2, 128, 1344), (16, 2, 128, 1344),
                                           (64, 8, 128, 1344), (4, 1, 64, 1344), (8, 2, 64, 1376),
