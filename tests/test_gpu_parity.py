@@ -30,7 +30,7 @@ def build_gpu(wl, chunks=None, kv=None):
     chunks = chunks or [max(wl.ctx)]
     pos = 0
     for n in chunks:
-        n = min(n, wl.cap - pos)
+        n = min(n, wl.cap - pos, max(wl.ctx) - pos)
         if n <= 0:
             break
         M.transform_quantize_append(cache, dev_input(k[:, :, pos:pos + n], wl.dtype),
@@ -99,6 +99,38 @@ def test_append_gqa_ragged(orc, chunks):
     g, a, b, k, v = build_gpu(wl, chunks)
     ref = build_oracle(orc, wl, k, v, b)
     assert_same_cache(planes_np(g), ref)
+
+
+def _random_append_cases(n: int, seed: int):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        d = int(rng.choice([64, 128]))
+        hkv = int(rng.integers(1, 4))
+        batch = int(rng.integers(1, 4))
+        cap = int(rng.integers(2, 40)) * 32
+        lens = [int(x) for x in rng.integers(0, cap + 40, size=batch)]   # some past capacity
+        chunks = []
+        while sum(chunks) < max(lens) + 8:
+            chunks.append(int(rng.choice([1, 1, 2, 3, 5, 31, 32, 33, 64, 200])))
+        dtype = "bf16" if rng.random() < 0.6 else "f32"
+        out.append((i, d, hkv, batch, cap, lens, chunks, dtype))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_append_cases(12, 77), ids=lambda c: f"a{c[0]}")
+def test_append_random_chunks(orc, case):
+    """Random chunk sequences (one-token, small and bulk appends, so both the
+    held-column and the bulk forms run) with ragged per-row counts, some rows
+    filled to the capacity: every plane byte-equal to the oracle's one-call
+    append of the same tokens."""
+    i, d, hkv, batch, cap, lens, chunks, dtype = case
+    ctx = [min(n, cap) for n in lens]
+    wl = W.custom(f"rapp{i}", 90 + i, batch, hkv, hkv, d, ctx, cap, dtype,
+                  log_uniform_key_scales=(dtype == "bf16"))
+    say("append random", i, "d", d, "hkv", hkv, "cap", cap, "lens", ctx, "chunks", chunks[:6], dtype)
+    g, a, b, k, v = build_gpu(wl, chunks)
+    assert_same_cache(planes_np(g), build_oracle(orc, wl, k, v, b))
 
 
 @pytest.mark.parametrize("d", [64, 128])
