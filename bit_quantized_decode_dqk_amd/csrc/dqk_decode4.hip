@@ -66,7 +66,7 @@ constexpr int kThreads4 = 256;
 constexpr int kWaves4 = kThreads4 / 64;
 constexpr int kTile4 = 64;          // tokens per wavefront tile: two key groups
 constexpr int kBlock4 = kTile4 * kWaves4;   // tokens per workgroup block
-constexpr int kChunk4 = 10;         // blocks per chunk: logits of a chunk stay in registers
+constexpr int kChunk4 = kDecodeChunkBlocks;   // blocks per chunk: logits of a chunk stay in registers
 // one block more than a chunk runs as one chunk: the extra block is committed to
 // LDS buffer kChunk4 & 1 and its values use stage kChunk4 % 3 (blocks alternate
 // over the two buffers and the value tiles over three stages)
@@ -213,38 +213,19 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
   // blocks are shared out over the nsplit splits: evenly, or, when two workgroups
   // share each compute unit (ncu = ncu_q * units + ncu_r > 0: the number of
   // compute units, workgroup ids below it being the first on their unit),
-  // unevenly.  The first workgroup on a
-  // unit issues ahead of the second (older wavefronts win the issue arbitration)
-  // and would finish well before it, so the splits dispatched second take 7/8 of
-  // the average share and the first ones the rest, at most one chunk each (with
-  // between 4 and about 8 blocks per split on average).
+  // unevenly (uneven_shares).
   int blo, bhi;
   {
     // first-slot splits: items s * units + unit below ncu
     const int fs = ncu_q + ncu_r > 0 ? min(nsplit, ncu_q + (unit < ncu_r ? 1 : 0)) : 0;
-    const int ss = nsplit - fs;
     if (bps > 0) {
       blo = min(s * bps, nblk_all);
       bhi = min(blo + bps, nblk_all);
-    } else if (fs > 0 && ss > 0 && nblk_all >= 4 * nsplit && nblk_all <= kChunk4 * fs + 8 * ss) {
-      // second-slot splits: 7/8 of the average share, rounded down, all the same
-      // (raised if the first-slot splits would need more than a chunk each); the
-      // first-slot splits share the rest evenly, at most one chunk each.  The last
-      // split, which also works out the exact logits of an unfinished last key
-      // group, takes one block less when there is one.
-      // (32-bit arithmetic: here nblk_all <= 10 nsplit and nsplit <= 2 ncu, with
-      // ncu below 4096, so that every product stays below 2^31)
-      const int cut = len % kGroup != 0 ? 1 : 0;
-      const uint32_t wt = 9u * fs + 7u * ss;
-      const int a2 = max((int)((7u * (uint32_t)nblk_all) / wt), (nblk_all + cut - kChunk4 * fs + ss - 1) / ss);
-      const int t1 = nblk_all - a2 * ss + cut;
-      if (s < fs) {
-        blo = (int)(((uint32_t)t1 * (uint32_t)s) / (uint32_t)fs);
-        bhi = (int)(((uint32_t)t1 * (uint32_t)(s + 1)) / (uint32_t)fs);
-      } else {
-        blo = t1 + a2 * (s - fs);
-        bhi = s == nsplit - 1 ? nblk_all : blo + a2;
-      }
+    } else if (const SplitShares sh = uneven_shares(nblk_all, nsplit, fs, len % kGroup != 0 ? 1 : 0);
+               sh.second >= 0) {
+      const BlockRange r = uneven_split_range(sh, s, fs, nsplit, nblk_all);
+      blo = r.lo;
+      bhi = r.hi;
     } else if ((unsigned long long)nblk_all * (unsigned long long)nsplit < (1ull << 32)) {
       blo = (int)(((uint32_t)s * (uint32_t)nblk_all) / (uint32_t)nsplit);
       bhi = (int)(((uint32_t)(s + 1) * (uint32_t)nblk_all) / (uint32_t)nsplit);

@@ -51,6 +51,60 @@ inline DecodeSplit matrix_decode_split(int capacity, int workgroups) {
   return {balanced_decode_split(capacity, workgroups), true};
 }
 
+// Blocks of 256 tokens per chunk of the matrix-core decode: a chunk's logits
+// stay in registers; a share of kDecodeChunkBlocks + 1 blocks still runs as one
+// chunk, so n blocks take max(1, (n - 2) / kDecodeChunkBlocks + 1) chunks.
+constexpr int kDecodeChunkBlocks = 10;
+
+// Uneven shares of a row's nblk blocks over nsplit splits in the matrix-core
+// decode when two workgroups share each compute unit: fs first-slot splits
+// (dispatched first on their unit), the rest second-slot.  The first workgroup
+// on a unit issues ahead of the second (older wavefronts win the issue
+// arbitration) and would finish well before it, so the second-slot splits take
+// 7/8 of the average share, rounded down, all the same, and the first-slot
+// splits share the rest.  No split may need a chunk more than an even share:
+// with shares of one chunk the first-slot splits take at most a chunk's blocks
+// each, with longer shares at most a chunk's blocks per chunk of the even
+// share; the second-slot share is raised until the rest fits, and where it
+// would then exceed the even share the row is shared evenly (second = -1).
+// The last split takes one block less (cut = 1) when it also works out the
+// exact logits of an unfinished last key group.  Shares apply from 4 to 50
+// blocks per split on average.  The arithmetic is 32-bit: the library uses the
+// rule only with nsplit at most twice the compute units (below 4096) and fs at
+// least (nsplit - 1) / 2, so that every product stays below 2^32.  (constexpr:
+// the same function runs in the kernel and in the host-side checks.)
+struct SplitShares {
+  int second;        // blocks of each second-slot split (-1: share evenly)
+  int first_total;   // blocks of the fs first-slot splits together
+};
+constexpr SplitShares uneven_shares(int nblk, int nsplit, int fs, int cut) {
+  const int ss = nsplit - fs;
+  if (fs <= 0 || ss <= 0 || nblk < 4 * nsplit || nblk > 50 * nsplit) return {-1, 0};
+  const int e = (nblk + nsplit - 1) / nsplit;                        // the even share
+  const bool one = nblk <= kDecodeChunkBlocks * fs + 8 * ss;         // shares of one chunk
+  const int cap1 = one ? kDecodeChunkBlocks : kDecodeChunkBlocks * ((e - 2) / kDecodeChunkBlocks + 1);
+  const uint32_t wt = 9u * (uint32_t)fs + 7u * (uint32_t)ss;
+  const int w = (int)((7u * (uint32_t)nblk) / wt);
+  const int fit = (nblk + cut - cap1 * fs + ss - 1) / ss;
+  const int a2 = w > fit ? w : fit;
+  if (!one && a2 > e) return {-1, 0};
+  return {a2, nblk - a2 * ss + cut};
+}
+
+// Blocks [lo, hi) of split s under uneven shares: the first-slot splits share
+// their total evenly, the second-slot splits follow with sh.second blocks each
+// and the last one ends the row.
+struct BlockRange {
+  int lo, hi;
+};
+constexpr BlockRange uneven_split_range(SplitShares sh, int s, int fs, int nsplit, int nblk) {
+  if (s < fs)
+    return {(int)(((uint32_t)sh.first_total * (uint32_t)s) / (uint32_t)fs),
+            (int)(((uint32_t)sh.first_total * (uint32_t)(s + 1)) / (uint32_t)fs)};
+  const int lo = sh.first_total + sh.second * (s - fs);
+  return {lo, s == nsplit - 1 ? nblk : lo + sh.second};
+}
+
 // Default split of the general decode: about two workgroups per CU, splits of 256
 // tokens or more.  (One split of a 1024-token row, which needs no combine launch,
 // measured slower in a replayed step: 18.6 against 12.9 us for select + decode.)

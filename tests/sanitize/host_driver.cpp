@@ -149,6 +149,42 @@ int main() {
           const dqk_cache x = fake(batch, hkv, 128, cap);
           EXPECT(dqk_decode_workspace_bytes(&x, g * hkv, 0, &ws), DQK_OK);
         }
+
+  // The matrix-core decode's uneven shares (the function the kernel runs), over
+  // the first-slot counts the library produces (fs >= nsplit / 2, fs < nsplit):
+  // the splits partition the row in order, no split needs more chunks than an
+  // even share, and the 32-bit products stay in range.
+  {
+    auto chunks = [](int n) { return n <= 1 ? 1 : (n - 2) / dqk::kDecodeChunkBlocks + 1; };
+    long applied = 0, bad = 0;
+    for (int nsplit : {2, 3, 4, 5, 7, 8, 9, 15, 16, 17, 31, 32, 33, 63, 64, 65, 100, 128, 255, 256, 511,
+                       512, 1000, 2047, 4096, 8191})
+      for (int fs : {nsplit / 2, nsplit / 2 + 1, (3 * nsplit) / 4, nsplit - 1}) {
+        if (fs < nsplit / 2 || fs >= nsplit) continue;
+        const int step = nsplit < 64 ? 1 : nsplit / 32;
+        for (int nblk = 1; nblk <= 52 * nsplit; nblk += step)
+          for (int cut = 0; cut < 2; ++cut) {
+            const dqk::SplitShares sh = dqk::uneven_shares(nblk, nsplit, fs, cut);
+            if (sh.second < 0) continue;
+            ++applied;
+            const int even = (nblk + nsplit - 1) / nsplit;
+            bool ok = (unsigned long long)sh.first_total * (unsigned long long)fs < (1ull << 32) &&
+                      sh.first_total >= 0;
+            int pos = 0;
+            for (int s = 0; s < nsplit && ok; ++s) {
+              const dqk::BlockRange r = dqk::uneven_split_range(sh, s, fs, nsplit, nblk);
+              ok = r.lo == pos && r.hi >= r.lo && chunks(r.hi - r.lo) <= chunks(even);
+              pos = r.hi;
+            }
+            if (!ok || pos != nblk) {
+              if (++bad <= 5)
+                std::fprintf(stderr, "uneven shares: nblk %d nsplit %d fs %d cut %d\n", nblk, nsplit, fs, cut);
+            }
+          }
+      }
+    std::printf("uneven shares: %ld cases, %ld bad\n", applied, bad);
+    if (bad != 0 || applied == 0) ++g_failures;
+  }
   std::printf("launches %d, failures %d\n", g_launches, g_failures);
   return g_failures == 0 ? 0 : 1;
 }
