@@ -23,12 +23,19 @@ namespace appb {
 
 constexpr int kThreads = 256;
 
-template <int D>
+// BULK workgroups write the transformed keys over the new keys once every
+// thread is through with the transform (a smaller workgroup footprint, so that
+// more of them share a compute unit); the others keep both.
+template <int D, bool BULK>
 struct __attribute__((aligned(16))) AppendSmem {
-  float kx[kGroup][D];   // new keys of the group (fp32)
-  float kp[kGroup][D];   // transformed keys
-  float vx[kGroup][D];   // new values (fp32)
-  float v2s[kGroup][D / kGroup];  // 2*scale per (token, value group)
+  float kx[kGroup][D];                 // new keys of the group (fp32)
+  float kpo[BULK ? 1 : kGroup][D];     // transformed keys (not BULK)
+  float vx[kGroup][D];                 // new values (fp32)
+  float v2s[kGroup][D / kGroup];       // 2*scale per (token, value group)
+  __device__ __forceinline__ float (*kp())[D] {
+    if constexpr (BULK) return kx;
+    else return kpo;
+  }
 };
 
 template <bool BF16>
@@ -47,8 +54,9 @@ template <int D, bool BF16, bool BULK>
 __device__ __forceinline__ void store_group(const dqk_cache &c, int b, int g, int grp, int L, int n,
                                             const void *k_new, const void *v_new,
                                             const float (&bcol)[D], const float *__restrict__ bmat,
-                                            int max_new, AppendSmem<D> &sm) {
+                                            int max_new, AppendSmem<D, BULK> &sm) {
   const int tid = threadIdx.x;
+  float (*kp)[D] = sm.kp();
   const int lo = max(L, grp * kGroup);
   const int hi = min(L + n, grp * kGroup + kGroup);
   const int cnt = hi - lo;                    // new tokens in this group, 1..32
@@ -64,17 +72,39 @@ __device__ __forceinline__ void store_group(const dqk_cache &c, int b, int g, in
   uint32_t *wp = c.v_codes + (unit * (size_t)(c.capacity / 16) + (size_t)(wlo >> 4)) * D + vch;
   const uint32_t wold = *wp;
 
-  // two elements of k and of v per thread in flight; the second index is
-  // clamped to the last element, which is then written twice with the same
-  // value (no branch, so no load waits behind another)
-  for (int e0 = tid; e0 < cnt * D; e0 += 2 * kThreads) {
-    const int e1 = min(e0 + kThreads, cnt * D - 1);
-    const float k0 = load_in<BF16>(k_new, row0 + e0), v0 = load_in<BF16>(v_new, row0 + e0);
-    const float k1 = load_in<BF16>(k_new, row0 + e1), v1 = load_in<BF16>(v_new, row0 + e1);
-    sm.kx[e0 / D][e0 % D] = k0;
-    sm.vx[e0 / D][e0 % D] = v0;
-    sm.kx[e1 / D][e1 % D] = k1;
-    sm.vx[e1 / D][e1 % D] = v1;
+  if constexpr (BULK) {
+    // the whole group's inputs in one round trip: every load is issued before
+    // any is written to LDS (indices past the new tokens are clamped to the
+    // last element and not written)
+    constexpr int EPT = kGroup * D / kThreads;
+    float kv[EPT], vv[EPT];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+      const int ec = min(tid + kThreads * j, cnt * D - 1);
+      kv[j] = load_in<BF16>(k_new, row0 + ec);
+      vv[j] = load_in<BF16>(v_new, row0 + ec);
+    }
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+      const int e = tid + kThreads * j;
+      if (e < cnt * D) {
+        sm.kx[e / D][e % D] = kv[j];
+        sm.vx[e / D][e % D] = vv[j];
+      }
+    }
+  } else {
+    // two elements of k and of v per thread in flight; the second index is
+    // clamped to the last element, which is then written twice with the same
+    // value (no branch, so no load waits behind another)
+    for (int e0 = tid; e0 < cnt * D; e0 += 2 * kThreads) {
+      const int e1 = min(e0 + kThreads, cnt * D - 1);
+      const float k0 = load_in<BF16>(k_new, row0 + e0), v0 = load_in<BF16>(v_new, row0 + e0);
+      const float k1 = load_in<BF16>(k_new, row0 + e1), v1 = load_in<BF16>(v_new, row0 + e1);
+      sm.kx[e0 / D][e0 % D] = k0;
+      sm.vx[e0 / D][e0 % D] = v0;
+      sm.kx[e1 / D][e1 % D] = k1;
+      sm.vx[e1 / D][e1 % D] = v1;
+    }
   }
   __syncthreads();
 
@@ -112,11 +142,12 @@ __device__ __forceinline__ void store_group(const dqk_cache &c, int b, int g, in
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) bq[ii] = bn[ii];
     }
+    __syncthreads();   // every thread is through with the new keys, which the results overwrite
 #pragma unroll
     for (int rr = 0; rr < TPT; ++rr)
       if (tr + rr < cnt) {
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) sm.kp[tr + rr][cj + jj] = acc[rr][jj];
+        for (int jj = 0; jj < 4; ++jj) kp[tr + rr][cj + jj] = acc[rr][jj];
       }
   } else {
     constexpr int S = kThreads / D;           // token slots per channel
@@ -126,7 +157,7 @@ __device__ __forceinline__ void store_group(const dqk_cache &c, int b, int g, in
       float acc = 0.0f;
 #pragma unroll
       for (int i = 0; i < D; ++i) acc = __builtin_fmaf(sm.kx[r0][i], bcol[i], acc);
-      if (r0 < cnt) sm.kp[r0][j] = acc;
+      if (r0 < cnt) kp[r0][j] = acc;
     } else {
       // rows of B fetched kBRows at a time, the next batch in flight while the
       // current one is used (the FMA order per output is unchanged)
@@ -153,13 +184,13 @@ __device__ __forceinline__ void store_group(const dqk_cache &c, int b, int g, in
       }
 #pragma unroll
       for (int m = 0; m < R; ++m)
-        if (r0 + m * S < cnt) sm.kp[r0 + m * S][j] = acc[m];
+        if (r0 + m * S < cnt) kp[r0 + m * S][j] = acc[m];
     }
   }
   __syncthreads();
 
   uint16_t *ch0 = c.k_ch0 + unit * (size_t)c.capacity;
-  for (int r = tid; r < cnt; r += kThreads) ch0[lo + r] = f16_bits(sm.kp[r][0]);
+  for (int r = tid; r < cnt; r += kThreads) ch0[lo + r] = f16_bits(kp[r][0]);
 
   if (hi == grp * kGroup + kGroup) {
     // The group is complete: quantize channels 1..D-1 over its 32 tokens.
@@ -170,7 +201,7 @@ __device__ __forceinline__ void store_group(const dqk_cache &c, int b, int g, in
 #pragma unroll
       for (int r = 0; r < kGroup; ++r) {
         const int p = grp * kGroup + r;
-        x[r] = p < lo ? tail[(size_t)r * D + ch] : sm.kp[p - lo][ch];
+        x[r] = p < lo ? tail[(size_t)r * D + ch] : kp[p - lo][ch];
         mx = fmaxf(mx, fabsf(x[r]));
       }
       const uint16_t sb = f16_bits(mx / 3.0f);
@@ -188,7 +219,7 @@ __device__ __forceinline__ void store_group(const dqk_cache &c, int b, int g, in
   } else {
     float *tail = c.k_tail + unit * (size_t)kGroup * D;
     for (int e = tid; e < cnt * D; e += kThreads)
-      tail[(size_t)((lo + e / D) & 31) * D + e % D] = sm.kp[e / D][e % D];
+      tail[(size_t)((lo + e / D) & 31) * D + e % D] = kp[e / D][e % D];
   }
 
   // Value scales: one per (new token, 32-channel group).
@@ -224,7 +255,7 @@ __device__ __forceinline__ void append_block(int block, const dqk_cache &c, cons
                                              const void *v_new, const float *__restrict__ bmat,
                                              const int32_t *__restrict__ n_new, int max_new,
                                              int blocks_per_unit) {
-  __shared__ AppendSmem<D> sm;
+  __shared__ AppendSmem<D, BULK> sm;
   const int unit = block / blocks_per_unit;
   const int bi = block % blocks_per_unit;
   const int b = unit / c.num_kv_heads, g = unit % c.num_kv_heads;
