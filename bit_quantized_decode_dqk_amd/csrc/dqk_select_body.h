@@ -62,7 +62,6 @@ __device__ __forceinline__ void select_block(int block, const void *q,
                                              int keep, float *q_prime, int32_t *sel_idx) {
   constexpr int HPB = heads_per_block<D>(), NSUB = blocks_per_unit<D, G>();
   static_assert(HPB * D <= kThreads && HPB * 64 <= kThreads, "one thread group and one wave per head");
-  __shared__ float qs[HPB][D];
   constexpr int WPH = kThreads / 64 / HPB;      // wavefronts per head in the ranking
   constexpr int SL = D / WPH;                   // channels each wavefront compares against
   constexpr int CPL = D / 64;                   // channels per lane
@@ -75,34 +74,31 @@ __device__ __forceinline__ void select_block(int block, const void *q,
   const int j = threadIdx.x, wave = j >> 6;
   const int col = j % D, grp = j / D;                 // grp is uniform in a wavefront
   const int nh = min(HPB, G - h0);                    // heads of this workgroup
-  // The query value and the lane's whole column of A_g are loaded together:
-  // the setup is one round trip.  Thread groups without a head load nothing.
+  // The lane's whole column of A_g is loaded at once (thread groups without a
+  // head load nothing); the chain below consumes its rows in order as they land.
   float a[D];
   if (grp < nh) {
-    const size_t e = (row0 + grp) * D + col;
-    float qv;
-    if constexpr (BF16)
-      qv = bf16_value(static_cast<const uint16_t *>(q)[e]);
-    else
-      qv = static_cast<const float *>(q)[e];
     const float *acol = amat + (size_t)g * D * D + col;
 #pragma unroll
     for (int r = 0; r < D; ++r) a[r] = acol[(size_t)r * D];
-    qs[grp][col] = qv;
-    // A's column is used here so that its loads are issued before the
-    // barrier, together with the query load (A is read-only: the compiler
-    // would otherwise move them past the barrier, a second round trip)
-#pragma unroll
-    for (int r = 0; r < D; ++r) asm volatile("" ::"v"(a[r]));
   }
-  __syncthreads();
-  // the thread group's row of qs at a compile-time index (a runtime row makes
-  // the compiler hoist every LDS read of the chain at once)
+  // The query row is the same for every lane of the thread group: it is read
+  // from memory as the chain goes (uniform addresses, no LDS and no barrier), so
+  // that each FMA waits only for its own row of A and element of q.  (Staging q
+  // in LDS made every chain wait at a barrier for the whole column of A.)
   auto chain = [&](auto grp_c) {
     constexpr int GRP = decltype(grp_c)::value;
+    const size_t qrow = (row0 + GRP) * D;
     float acc = 0.0f;
 #pragma unroll
-    for (int r = 0; r < D; ++r) acc = __builtin_fmaf(qs[GRP][r], a[r], acc);
+    for (int r = 0; r < D; ++r) {
+      float qv;
+      if constexpr (BF16)
+        qv = bf16_value(static_cast<const uint16_t *>(q)[qrow + r]);
+      else
+        qv = static_cast<const float *>(q)[qrow + r];
+      acc = __builtin_fmaf(qv, a[r], acc);
+    }
     q_prime[(row0 + GRP) * D + col] = acc;
     key[GRP][col] = order_key<D>(acc, col);
   };
