@@ -281,7 +281,7 @@ def main():
         print(f"source_hash: {kernel_source_hash()}")
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
