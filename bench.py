@@ -81,6 +81,8 @@ def append_bytes(batch: int, hkv: int, d: int, positions, in_bytes: int) -> int:
 # ----------------------------------------------------------------------------- profiles
 
 KERNEL_SOURCES = ("bit_quantized_decode_dqk_amd/csrc/dqk_decode.hip",
+                  "bit_quantized_decode_dqk_amd/csrc/dqk_decode8.hip",
+                  "bit_quantized_decode_dqk_amd/csrc/dqk_host.h",
                   "bit_quantized_decode_dqk_amd/csrc/dqk_decode4.hip",
                   "bit_quantized_decode_dqk_amd/csrc/dqk_decode_ops.h",
                   "bit_quantized_decode_dqk_amd/csrc/dqk_combine.hip",

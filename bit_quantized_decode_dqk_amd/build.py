@@ -31,6 +31,7 @@ SOURCES = {
     # the chunk loops (up to ten blocks, with a run-time exit) must unroll fully,
     # or the chunk's logits would be indexed at run time and go to scratch memory
     "dqk_decode4.hip": ["-fno-honor-nans", "-mllvm", "-unroll-max-upperbound=16"],
+    "dqk_decode8.hip": ["-fno-honor-nans", "-mllvm", "-unroll-max-upperbound=16"],
     "dqk_bf16.hip": [],
     "dqk_combine.hip": [],
     "dqk_probe.hip": [],

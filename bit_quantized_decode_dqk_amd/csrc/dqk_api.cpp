@@ -56,7 +56,9 @@ int decode_split(const dqk_cache *c, int hq, int split, bool *even = nullptr) {
   const int units = c->batch * c->num_kv_heads;
   if (hq % (4 * c->num_kv_heads) != 0) return dqk::default_decode_split(c->capacity, units);
   const dqk::DecodeSplit d =
-      dqk::matrix_decode_split(c->capacity, units * (hq / (4 * c->num_kv_heads)));
+      hq == 8 * c->num_kv_heads && c->capacity % 64 == 0
+          ? dqk::matrix_decode_split8(c->capacity, units)
+          : dqk::matrix_decode_split(c->capacity, units * (hq / (4 * c->num_kv_heads)));
   if (even) *even = d.even;
   return d.split;
 }

@@ -614,8 +614,12 @@ hipError_t launch_decode_d(const dqk_cache &c, const float *qp, const int32_t *s
                    : launch_decode_t<D, 8>(c, qp, sel, shared, hq, keep, scale2, split, out, ws, s);
       const int nsplit = num_splits(c.capacity, split);
       // one split per row: the kernel writes the output itself and no combine runs
+      // (groups of eight with per-head kept sets: one workgroup for the eight heads)
       const hipError_t e =
-          launch_decode4(c, qp, sel, shared != 0, hq, keep, scale2, split, even, ws, nsplit == 1 ? out : nullptr, s);
+          !shared && decode8_supported(c, hq)
+              ? launch_decode8(c, qp, sel, hq, keep, scale2, split, even, ws, nsplit == 1 ? out : nullptr, s)
+              : launch_decode4(c, qp, sel, shared != 0, hq, keep, scale2, split, even, ws,
+                               nsplit == 1 ? out : nullptr, s);
       if (e != hipSuccess || nsplit == 1) return e;
       return launch_combine(ws, c.batch, hq, c.num_kv_heads, D, nsplit, out, s);
     }

@@ -51,6 +51,18 @@ inline DecodeSplit matrix_decode_split(int capacity, int workgroups) {
   return {balanced_decode_split(capacity, workgroups), true};
 }
 
+// Default split of the eight-head matrix-core decode (one workgroup per work
+// item, blocks of 128 tokens, the same chunks of ten blocks): the rule above in
+// its blocks -- fixed splits of kFixedSplitBlocks8 whole blocks when the capacity
+// alone gives more than that many per resident workgroup slot, else the balanced
+// split count with equal (or uneven, two workgroups per compute unit) shares.
+constexpr int kFixedSplitBlocks8 = 31;
+inline DecodeSplit matrix_decode_split8(int capacity, int units) {
+  const long long blocks = (long long)units * ((capacity + 127) / 128);
+  if (blocks > (long long)kFixedSplitBlocks8 * 512) return {kFixedSplitBlocks8 * 128, false};
+  return {balanced_decode_split(capacity, units), true};
+}
+
 // Blocks of 256 tokens per chunk of the matrix-core decode: a chunk's logits
 // stay in registers; a share of kDecodeChunkBlocks + 1 blocks still runs as one
 // chunk, so n blocks take max(1, (n - 2) / kDecodeChunkBlocks + 1) chunks.
@@ -149,6 +161,11 @@ bool decode4_supported(const dqk_cache &c, int hq);
 hipError_t launch_decode4(const dqk_cache &c, const float *q_prime, const int32_t *sel_idx,
                           bool shared, int hq, int keep, float scale2, int split, bool even,
                           float *ws, float *out, hipStream_t s);
+// the eight-head decode: hq == 8 hkv, per-head kept sets, capacity a multiple of 64
+bool decode8_supported(const dqk_cache &c, int hq);
+hipError_t launch_decode8(const dqk_cache &c, const float *q_prime, const int32_t *sel_idx, int hq,
+                          int keep, float scale2, int split, bool even, float *ws, float *out,
+                          hipStream_t s);
 hipError_t launch_dequant(const dqk_cache &c, float *k_out, float *v_out, hipStream_t s);
 // every plane of src re-strided into dst (same batch, KV heads, head_dim; larger capacity)
 hipError_t launch_cache_grow(const dqk_cache &src, const dqk_cache &dst, hipStream_t s);
