@@ -162,8 +162,9 @@ dqk_status dqk_decode_workspace_bytes(const dqk_cache *cache, int32_t hq,
  * library's choice) fixes the number of splits, ceil(capacity / split_tokens).
  * For groups of 4 or 8 query heads per KV head and a capacity that is a multiple of
  * 64, the products run on the matrix cores with fp32 accumulation; there a multiple
- * of 256 gives each split exactly its split_tokens tokens of every row, and other
- * values share each row's current 256-token blocks out over the splits.  Otherwise
+ * of the kernel's block (256 tokens for groups of 4, 128 for groups of 8) gives each
+ * split exactly its split_tokens tokens of every row, and other values share each
+ * row's current blocks out over the splits.  Otherwise
  * split s covers tokens [s split_tokens, (s + 1) split_tokens).  The result does not
  * depend on the split beyond fp32 rounding.  With a single split (split_tokens >=
  * capacity) the decode writes out itself and the workspace is not touched.
