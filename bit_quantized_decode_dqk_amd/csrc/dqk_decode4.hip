@@ -617,6 +617,10 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
   const uint32_t vwv = (uint32_t)(16 * q + n) * 4u;                   // word row 0, channel 16q + n of the tile
   const uint32_t vsv = (uint32_t)(32 * lg + 2 * n) * (uint32_t)(L::VG * 2);   // scales of my two tokens
 
+  // Values are read once: their loads carry the non-temporal hint, so that they
+  // do not push out of L2 the key lines a block shares with the next one (a key
+  // block uses half of each 128-byte line of its channels' codes).
+  constexpr int kNT = 2;
   auto vissue = [&](VStage4<D> &V, int tile0, bool live) {
     __builtin_amdgcn_sched_barrier(0);
     live = live && tile0 < t_end;
@@ -627,12 +631,12 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
     for (int hf = 0; hf < L::NH; ++hf)
 #pragma unroll
       for (int wr = 0; wr < 4; ++wr)
-        V.vw[hf][wr] = __builtin_amdgcn_raw_buffer_load_b32(rvw, vwv + (uint32_t)(wr * D + 64 * hf) * 4u, 0, 0);
+        V.vw[hf][wr] = __builtin_amdgcn_raw_buffer_load_b32(rvw, vwv + (uint32_t)(wr * D + 64 * hf) * 4u, 0, kNT);
     if constexpr (L::VG == 4) {
-      const u32x4 x = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rvs, vsv, 0, 0));
+      const u32x4 x = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rvs, vsv, 0, kNT));
       V.vs[0] = x.x; V.vs[1] = x.y; V.vs[2] = x.z; V.vs[3] = x.w;
     } else {
-      const u32x2 x = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rvs, vsv, 0, 0));
+      const u32x2 x = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rvs, vsv, 0, kNT));
       V.vs[0] = x.x; V.vs[1] = x.y;
     }
     __builtin_amdgcn_sched_barrier(0);
