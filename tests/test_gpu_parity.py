@@ -324,13 +324,15 @@ def test_decode_group4_empty_and_short_rows(orc, hq):
     decode_case(orc, wl, sparsity=0, sm_mult=0.02, splits=(0,))
 
 
-def test_decode4_many_splits_one_dimensional_grid(orc):
+@pytest.mark.parametrize("hq", [4, 8])
+def test_decode4_many_splits_one_dimensional_grid(orc, hq):
     """65538 splits of a row (32-token splits over a 2M-token capacity) do not fit
-    the (KV head, row, split) grid of the matrix-core decode: its work items are
-    then numbered on a one-dimensional grid.  Most splits are empty; the result
-    must match the oracle as for the default split and a 4096-token one."""
+    the (KV head, row, split) grid of the matrix-core decodes (four and eight
+    heads per workgroup): their work items are then numbered on a one-dimensional
+    grid.  Most splits are empty; the result must match the oracle as for the
+    default split and a 4096-token one."""
     cap = 2097216   # a multiple of 64; ceil(cap / 32) = 65538 splits
-    wl = W.custom("many-splits", 61, 1, 4, 1, 64, [5000], cap, "bf16", log_uniform_key_scales=True)
+    wl = W.custom(f"many-splits{hq}", 61, 1, hq, 1, 64, [5000], cap, "bf16", log_uniform_key_scales=True)
     decode_case(orc, wl, splits=(32, 0, 4096))
 
 
