@@ -32,6 +32,8 @@ def test_noalloc_decode_matches_workspace_decode():
                   log_uniform_key_scales=True), 0),         # matrix-core kernel, default split
         (W.custom("na-g4b", 91, 2, 32, 8, 128, [3000, 0], 3008, "bf16",
                   log_uniform_key_scales=True), 512),       # smaller, a fixed split, an empty row
+        (W.custom("na-g8", 93, 2, 16, 2, 128, [2500, 700], 2560, "bf16",
+                  log_uniform_key_scales=True), 0),         # the eight-head kernel, smaller
         (W.custom("na-g2", 92, 2, 4, 2, 64, [700, 31], 768, "f32"), 0),   # general kernel, smaller
     ]
     sm = W.default_sm_scale(128)
