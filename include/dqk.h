@@ -17,7 +17,9 @@
  *    returning.  Its only process state is a per-device cache of the compute
  *    unit count (queried once per device on first use by the decode, never
  *    freed; it changes no result, only how a row's blocks are shared out over
- *    the splits).  Calls are thread-safe.
+ *    the splits) and, for dqk_decode_attention_noalloc only, that call's
+ *    per-device scratch array and its looked-up address (below).  Calls are
+ *    thread-safe, except that noalloc calls overlapping on one GPU race.
  *  - Work is enqueued on `stream` (0 = the null stream); no call synchronizes.
  *  - Every argument the host can see is validated before anything is launched:
  *    an invalid call returns an error status and launches nothing.  A launch
