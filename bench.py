@@ -257,6 +257,18 @@ def cpu_baseline(wl, a, b, keep, sm, budget_s: float = 20.0):
 
 # ----------------------------------------------------------------------------- GPU
 
+def calibration_copy(torch, mib: int) -> None:
+    """A device-to-device copy of a known size (three times), the reference that
+    scales the HBM byte counters of a profiled run (summarize_rocprof)."""
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -293,6 +305,8 @@ def main():
     torch.cuda.set_device(0)
     if args.only_workload:
         print(json.dumps(run_configs(M, torch, names=(args.only_workload,))), flush=True)
+        if args.calibrate_copy_mib > 0:
+            calibration_copy(torch, args.calibrate_copy_mib)
         return
     dev = "cuda"
     wl = W.workload("ctx128k", steps=256)
@@ -433,13 +447,7 @@ def main():
         log(f"graph-replayed step {ms_step * 1e3:.1f} us, {gbs:.0f} GB/s step")
 
     if args.calibrate_copy_mib > 0:
-        n = args.calibrate_copy_mib << 20
-        src = torch.ones(n, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        calibration_copy(torch, args.calibrate_copy_mib)
 
     # The dominant kernel pair for the roofline: the decode alone, launched back to back
     # (in the eager step loop the host launches trail the GPU, so the in-step events also
@@ -836,7 +844,8 @@ def run_configs(M, torch, steps: int = 32, names=("tiny", "gqa8k", "append32k", 
             if appends:
                 nb += append_bytes(wl.batch, wl.hkv, wl.d, lengths[ci], inb)
                 lengths[ci] = lengths[ci] + 1
-            return nb + decode_bytes(idx.cpu().numpy(), lengths[ci], wl.hkv, wl.d, keep)
+            db = decode_bytes(idx.cpu().numpy(), lengths[ci], wl.hkv, wl.d, keep)
+            return nb + db, db
 
         def step(i):
             c = caches[i % len(caches)]
@@ -859,7 +868,8 @@ def run_configs(M, torch, steps: int = 32, names=("tiny", "gqa8k", "append32k", 
         for i in range(1, n + 1):                 # lengths after the untimed replay
             if appends:
                 lengths[i % len(caches)] = lengths[i % len(caches)] + 1
-        tot = sum(advance(i) for i in range(1, n + 1))
+        per = [advance(i) for i in range(1, n + 1)]
+        tot, dec_tot = sum(x[0] for x in per), sum(x[1] for x in per)
         torch.cuda.synchronize()
         ts = time.perf_counter()
         graph.replay()
@@ -868,7 +878,8 @@ def run_configs(M, torch, steps: int = 32, names=("tiny", "gqa8k", "append32k", 
         us = 1e6 * wall / n
         res[name] = {"us_per_step": round(us, 2), "GB/s": round(tot / wall / 1e9, 1),
                      "tokens_per_s": round(wl.batch / (us * 1e-6), 1),
-                     "bytes_per_step": int(tot / n), "steps": n, "cache_copies": len(caches),
+                     "bytes_per_step": int(tot / n), "decode_bytes_per_step": int(dec_tot / n),
+                     "steps": n, "cache_copies": len(caches),
                      "step": ("append 1 + select + decode" if appends else "select + decode"),
                      "workload": wl.describe()}
         log(f"{name}: {us:.1f} us/step, {tot / wall / 1e9:.0f} GB/s "

@@ -443,14 +443,16 @@ def test_decode_group4_chunk_sizes(orc):
                                           (20, 5, [1800, 4000]), (8, 1, [3000, 1200, 64]),
                                           (24, 3, [2500]), (40, 5, [1800, 4000])])
 def test_decode_group4_unit_counts(orc, hq, hkv, lens):
-    """Groups of four (and of eight, two four-head workgroups per split) with
-    (row, KV head) counts that are not multiples of eight: the splits of one row
-    and KV head run on different parts of the chip, the grid of a group of eight
-    is padded to whole groups of eight work items, and the combine joins the
-    partials."""
+    """Groups of four and of eight with (row, KV head) counts that are not
+    multiples of eight: the splits of one row and KV head run on different parts
+    of the chip, and the combine joins the partials.  Groups of eight also run
+    with group-shared kept sets: two four-head workgroups per work item, with the
+    grid padded to whole groups of eight work items."""
     wl = W.custom(f"g4-u{hkv}", 30 + hkv, len(lens), hq, hkv, 128, lens, 4032, "bf16",
                   log_uniform_key_scales=True)
     decode_case(orc, wl, splits=(0, 64, 256, 1024))
+    if hq == 8 * hkv:
+        decode_shared_case(orc, wl, splits=(0, 64, 1024))
 
 
 def test_decode_workspace_reuse(orc):
