@@ -58,7 +58,7 @@ int decode_split(const dqk_cache *c, int hq, int split, bool *even = nullptr) {
   const dqk::DecodeSplit d =
       hq == 8 * c->num_kv_heads && c->capacity % 64 == 0
           ? dqk::matrix_decode_split8(c->capacity, units)
-          : dqk::matrix_decode_split(c->capacity, units * (hq / (4 * c->num_kv_heads)));
+          : dqk::matrix_decode_split(c->capacity, units);
   if (even) *even = d.even;
   return d.split;
 }

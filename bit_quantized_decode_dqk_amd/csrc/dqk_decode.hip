@@ -608,18 +608,17 @@ hipError_t launch_decode_d(const dqk_cache &c, const float *qp, const int32_t *s
     case 2: return launch_decode_t<D, 2>(c, qp, sel, shared, hq, keep, scale2, split, out, ws, s);
     case 4:
     case 8: {
-      if (!decode4_supported(c, hq))
-        return hq == 4 * c.num_kv_heads
-                   ? launch_decode_t<D, 4>(c, qp, sel, shared, hq, keep, scale2, split, out, ws, s)
-                   : launch_decode_t<D, 8>(c, qp, sel, shared, hq, keep, scale2, split, out, ws, s);
+      // the matrix-core decodes (one workgroup for the four or eight heads of a KV
+      // head) need a capacity that is a multiple of 64 tokens
+      const bool eight = hq == 8 * c.num_kv_heads;
+      if (!(eight ? decode8_supported(c, hq) : decode4_supported(c, hq)))
+        return eight ? launch_decode_t<D, 8>(c, qp, sel, shared, hq, keep, scale2, split, out, ws, s)
+                     : launch_decode_t<D, 4>(c, qp, sel, shared, hq, keep, scale2, split, out, ws, s);
       const int nsplit = num_splits(c.capacity, split);
       // one split per row: the kernel writes the output itself and no combine runs
-      // (groups of eight with per-head kept sets: one workgroup for the eight heads)
-      const hipError_t e =
-          !shared && decode8_supported(c, hq)
-              ? launch_decode8(c, qp, sel, hq, keep, scale2, split, even, ws, nsplit == 1 ? out : nullptr, s)
-              : launch_decode4(c, qp, sel, shared != 0, hq, keep, scale2, split, even, ws,
-                               nsplit == 1 ? out : nullptr, s);
+      float *o = nsplit == 1 ? out : nullptr;
+      const hipError_t e = eight ? launch_decode8(c, qp, sel, shared != 0, hq, keep, scale2, split, even, ws, o, s)
+                                 : launch_decode4(c, qp, sel, shared != 0, hq, keep, scale2, split, even, ws, o, s);
       if (e != hipSuccess || nsplit == 1) return e;
       return launch_combine(ws, c.batch, hq, c.num_kv_heads, D, nsplit, out, s);
     }

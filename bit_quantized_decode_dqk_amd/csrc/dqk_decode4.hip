@@ -1,6 +1,5 @@
 // Decode attention over the 2-bit cache for GQA groups of four query heads
-// (hq / hkv == 4, or a multiple of four served four heads per workgroup), both
-// contractions on the matrix cores.
+// (hq / hkv == 4), both contractions on the matrix cores.
 //
 // Dual-QK (arXiv abstract; tech.dede.sh summary, "Throughput on SGLang"): keys
 // and values are stored in 2 bits and the key channels a query head does not
@@ -26,7 +25,7 @@
 //     logits of the block's 64-token tile w and keeps them in registers.
 //  2. values.  With the exact maximum of its logits in the chunk known, every
 //     wavefront streams the value words and scales of its own tiles straight
-//     into registers (two tiles in flight, no barrier) and accumulates the
+//     into registers (three tiles in flight, no barrier) and accumulates the
 //     weighted sum.  Only a later chunk with a larger maximum rescales what was
 //     accumulated.
 //
@@ -43,8 +42,9 @@
 //    Then z = 2^(E_h + 25 - 2k) (C_high + C_low) - 3 2^E_h (C1_high + C1_low) + ch0 term.
 //  - values, per 32 tokens and 16 channels of value group j: A[h][t] =
 //    p_{h,t} scale_{t,j} 2^(F + 24 - 2k(t)) in fp16 (p = 2^(z - max) <= 1, F a
-//    power of two that keeps A below 2^15), B[t][c] = u 2^(2k-24); a product
-//    with B = 2^(2k-24) gives S = 2^F sum p scale, and out = 2^-F (2 C - 3 S).
+//    power of two that keeps A below 2^15), B[t][c] = u 2^(2k-24); beside the
+//    product, mixed-precision FMAs sum S = 2^F sum p scale from the same fp16
+//    operands, and out = 2^-F (2 C - 3 S).
 //    F moves (and what was accumulated is rescaled by a power of two) only when
 //    a value scale outgrows the range it allows.
 //
@@ -61,7 +61,7 @@ namespace {
 using namespace wave;
 using namespace dops;
 
-constexpr int kG4 = 4;              // query heads per workgroup (a slice of the KV head's group)
+constexpr int kG4 = 4;              // query heads per workgroup: the KV head's group
 constexpr int kThreads4 = 256;
 constexpr int kWaves4 = kThreads4 / 64;
 constexpr int kTile4 = 64;          // tokens per wavefront tile: two key groups
@@ -151,7 +151,7 @@ template <int D, bool COMPACT>
 __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
                                                                const float *__restrict__ qp,
                                                                const int32_t *__restrict__ sel,
-                                                               int shared, int hq, int nsl, int grid3, int keep,
+                                                               int shared, int hq, int grid3, int keep,
                                                                float scale2, int nsplit, int bps, int ncu_q,
                                                                int ncu_r, int nkc, float *__restrict__ ws,
                                                                float *__restrict__ out) {
@@ -161,24 +161,19 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: block and tile offsets stay scalar
   // Work item (unit, split s) in split-major order: workgroups of one split index
-  // run together.  With one slice of four query heads per KV head (nsl == 1) the
-  // grid is (KV head, row, split) where it fits (grid3), so that the linear
-  // workgroup id is the item s * units + unit and no division stands between the
-  // start and the length load.  Otherwise the grid is one-dimensional; a KV head
-  // with more than four query heads is then served in nsl slices of four, one
-  // workgroup each, and the slices of one work item get workgroup ids eight apart,
-  // which go to the same XCD (workgroups are dealt round-robin over the eight
-  // XCDs), so a later slice finds the item's bytes in that XCD's L2.
+  // run together.  The grid is (KV head, row, split) where it fits (grid3), so
+  // that the linear workgroup id is the item s * units + unit and no division
+  // stands between the start and the length load; otherwise it is
+  // one-dimensional over the items.
   const int units = c.batch * c.num_kv_heads;
-  int b, g, s, slice = 0;
+  int b, g, s;
   if (grid3) {
     g = blockIdx.x;
     b = blockIdx.y;
     s = blockIdx.z;
   } else {
-    slice = (blockIdx.x >> 3) % nsl;
-    const int item = (blockIdx.x / (8 * nsl)) * 8 + (blockIdx.x & 7);
-    if (item >= units * nsplit) return;   // the grid is padded to whole groups of eight items
+    const int item = blockIdx.x;
+    if (item >= units * nsplit) return;
     const int unit = item % units;
     s = item / units;
     b = unit / c.num_kv_heads;
@@ -186,9 +181,9 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
   }
   const int unit = b * c.num_kv_heads + g;
   const int len = max(0, min(c.lengths[b], c.capacity));
-  // The slice's q' rows (all channels) and kept-channel lists are loaded before
+  // The group's q' rows (all channels) and kept-channel lists are loaded before
   // anything waits, in parallel with the length: one round trip for the setup.
-  const size_t row0 = (size_t)b * hq + (size_t)g * G * nsl + (size_t)G * slice;
+  const size_t row0 = (size_t)b * hq + (size_t)g * G;
   constexpr int SJ = (G * D) / kThreads4;   // elements per lane
   float qv[SJ];
   int sv[SJ];
@@ -237,7 +232,7 @@ __global__ __launch_bounds__(kThreads4, 2) void decode4_kernel(dqk_cache c,
   const int t_begin = blo * kBlock4;
   const int t_end = min(bhi * kBlock4, len);
   const int nb = bhi - blo;
-  float *wsp = ws + (((size_t)unit * nsplit + s) * nsl + slice) * G * (D + kPartialHead);
+  float *wsp = ws + ((size_t)unit * nsplit + s) * G * (D + kPartialHead);
   // out != nullptr: a single split per row, whose normalized output is written
   // directly (what the combine makes of one partial); an empty row gives zeros
   float *outp = out ? out + row0 * D : nullptr;
@@ -979,7 +974,7 @@ int compute_units() {
 }
 
 bool decode4_supported(const dqk_cache &c, int hq) {
-  return c.capacity % 64 == 0 && hq % (c.num_kv_heads * kG4) == 0;
+  return c.capacity % 64 == 0 && hq == kG4 * c.num_kv_heads;
 }
 
 hipError_t launch_decode4(const dqk_cache &c, const float *q_prime, const int32_t *sel_idx,
@@ -992,19 +987,16 @@ hipError_t launch_decode4(const dqk_cache &c, const float *q_prime, const int32_
   const int bps = !even && split % kBlock4 == 0 ? split / kBlock4 : 0;
   const int units = c.batch * c.num_kv_heads;
   const int items = units * nsplit;
-  const int nsl = hq / (c.num_kv_heads * kG4);
-  // one slice per KV head: (KV head, row, split), whose linear order is the item
-  // order, if rows and splits fit the grid's second and third dimensions; else
-  // the padded one-dimensional grid (of the slices)
-  const int grid3 = nsl == 1 && c.batch <= 65535 && nsplit <= 65535 ? 1 : 0;
+  // (KV head, row, split), whose linear order is the item order, if rows and
+  // splits fit the grid's second and third dimensions; else one-dimensional
+  const int grid3 = c.batch <= 65535 && nsplit <= 65535 ? 1 : 0;
   const dim3 grid = grid3 ? dim3((unsigned)c.num_kv_heads, (unsigned)c.batch, (unsigned)nsplit)
-                          : dim3((unsigned)((items + 7) / 8 * 8 * nsl));
+                          : dim3((unsigned)items);
   const dim3 block(kThreads4);
-  // uneven shares for two workgroups per compute unit (the library's own split of
-  // groups of four only; the kernel's share arithmetic is 32-bit for fewer than
-  // 4096 compute units)
+  // uneven shares for two workgroups per compute unit (the library's own split
+  // only; the kernel's share arithmetic is 32-bit for fewer than 4096 compute units)
   int ncu = 0;
-  if (even && nsl == 1 && bps == 0) {
+  if (even && bps == 0) {
     const int n = compute_units();
     if (n > 0 && n < 4096 && items > n && items <= 2 * n) ncu = n;
   }
@@ -1015,17 +1007,17 @@ hipError_t launch_decode4(const dqk_cache &c, const float *q_prime, const int32_
   const int sh = shared ? 1 : 0;
   if (c.head_dim == 64) {
     if (shared)
-      hipLaunchKernelGGL((decode4_kernel<64, true>), grid, block, 0, s, c, q_prime, sel_idx, sh, hq, nsl, grid3, keep,
+      hipLaunchKernelGGL((decode4_kernel<64, true>), grid, block, 0, s, c, q_prime, sel_idx, sh, hq, grid3, keep,
                          scale2, nsplit, bps, ncu_q, ncu_r, nkc, ws, out);
     else
-      hipLaunchKernelGGL((decode4_kernel<64, false>), grid, block, 0, s, c, q_prime, sel_idx, sh, hq, nsl, grid3, keep,
+      hipLaunchKernelGGL((decode4_kernel<64, false>), grid, block, 0, s, c, q_prime, sel_idx, sh, hq, grid3, keep,
                          scale2, nsplit, bps, ncu_q, ncu_r, nkc, ws, out);
   } else {
     if (shared)
-      hipLaunchKernelGGL((decode4_kernel<128, true>), grid, block, 0, s, c, q_prime, sel_idx, sh, hq, nsl, grid3, keep,
+      hipLaunchKernelGGL((decode4_kernel<128, true>), grid, block, 0, s, c, q_prime, sel_idx, sh, hq, grid3, keep,
                          scale2, nsplit, bps, ncu_q, ncu_r, nkc, ws, out);
     else
-      hipLaunchKernelGGL((decode4_kernel<128, false>), grid, block, 0, s, c, q_prime, sel_idx, sh, hq, nsl, grid3, keep,
+      hipLaunchKernelGGL((decode4_kernel<128, false>), grid, block, 0, s, c, q_prime, sel_idx, sh, hq, grid3, keep,
                          scale2, nsplit, bps, ncu_q, ncu_r, nkc, ws, out);
   }
   return hipGetLastError();

@@ -1,7 +1,7 @@
 // Decode attention over the 2-bit cache for GQA groups of eight query heads
-// (hq / hkv == 8) with per-head kept sets: one workgroup serves all eight heads
-// of a KV head, so each key and value byte is read once and each 2-bit code is
-// turned into a matrix-core operand once for the eight heads.
+// (hq / hkv == 8), with per-head or group-shared kept sets: one workgroup serves
+// all eight heads of a KV head, so each key and value byte is read once and each
+// 2-bit code is turned into a matrix-core operand once for the eight heads.
 //
 // Dual-QK (arXiv abstract; tech.dede.sh summary, "Throughput on SGLang"): keys
 // and values are stored in 2 bits and the key channels no head of the group
@@ -97,6 +97,7 @@ struct __attribute__((aligned(16))) Smem8 {
     uint32_t w[kG8 * D / 4];
   } kept;
   unsigned long long umask[2];   // the union U of kept key channels >= 1
+  int32_t ulist[D];              // compact slots: key channel of slot i (-1 past |U|)
 };
 
 // Registers of one block of keys in flight.
@@ -118,13 +119,17 @@ __device__ __forceinline__ float sel4(int q, float a0, float a1, float a2, float
   return sel2((q & 2) != 0, sel2((q & 1) != 0, a0, a1), sel2((q & 1) != 0, a2, a3));
 }
 
-template <int D>
+// COMPACT (group-shared kept sets, one per KV head): union slot i holds the
+// i-th kept key channel other than 0, and only the nkc K chunks that hold the
+// keep - 1 such channels are worked on; otherwise slot i holds channel i + 1 and
+// all K chunks run.
+template <int D, bool COMPACT>
 __global__ __launch_bounds__(kThreads8, 2) void decode8_kernel(dqk_cache c,
                                                                const float *__restrict__ qp,
                                                                const int32_t *__restrict__ sel,
                                                                int hq, int grid3, int keep, float scale2,
                                                                int nsplit, int bps, int ncu_q, int ncu_r,
-                                                               float *__restrict__ ws,
+                                                               int nkc, float *__restrict__ ws,
                                                                float *__restrict__ out) {
   using L = Lay8<D>;
   constexpr int G = kG8;
@@ -158,7 +163,21 @@ __global__ __launch_bounds__(kThreads8, 2) void decode8_kernel(dqk_cache c,
   for (int k = 0; k < SJ; ++k) {
     const int e = tid + kThreads8 * k;
     qv[k] = qp[row0 * D + e];
-    sv[k] = e < G * keep ? sel[row0 * keep + e] : -1;
+    // the head's kept set: its own row, or its KV head's shared one (position
+    // e mod keep, by subtraction: e < G keep)
+    if constexpr (COMPACT) {
+      int es = e;
+#pragma unroll
+      for (int h = 1; h < G; ++h) es = es >= keep ? es - keep : es;
+      sv[k] = e < G * keep ? sel[(size_t)unit * keep + es] : -1;
+    } else {
+      sv[k] = e < G * keep ? sel[row0 * keep + e] : -1;
+    }
+  }
+  // compact slots: the shared kept list without channel 0, one slot per lane
+  int uch = -1;
+  if constexpr (COMPACT) {
+    if (tid < D && tid + 1 < keep) uch = sel[(size_t)unit * keep + tid + 1];
   }
   const int nblk_all = (len + kBlock8 - 1) / kBlock8;
   // bps > 0: split s is blocks [s bps, (s + 1) bps).  Else the row's blocks are
@@ -231,8 +250,10 @@ __global__ __launch_bounds__(kThreads8, 2) void decode8_kernel(dqk_cache c,
   }
 
   // ---------------------------------------------------------------- key loads (every lane)
-  // Union slot i holds key channel i + 1 (the last slot is empty); the first
-  // block is issued for every channel, later blocks for the union only.
+  // Union slot i holds key channel i + 1 (the last slot is empty): the first
+  // block is issued for every channel as soon as the length is known, later
+  // blocks for the union only.  Compact slots hold the shared set's channels:
+  // the first block is issued once the set is in LDS, for those channels only.
   auto mul_apart = [](uint32_t a, uint32_t b2) {
     uint32_t p = a * b2;
     asm volatile("" : "+v"(p));
@@ -249,18 +270,22 @@ __global__ __launch_bounds__(kThreads8, 2) void decode8_kernel(dqk_cache c,
   const int aj = tid % (kWaves8 * L::SPJ), at = aj & 3, asp = aj >> 2;
   const int aoct = asp >> 2, am = asp & 3;
   const int as0 = 8 * aoct + (am & 1) + 4 * (am >> 1), as1 = as0 + 2;
-  auto slot_channel = [&](int i) -> int { return i + 1 < D ? i + 1 : -1; };
+  auto slot_channel = [&](int i) -> int {
+    if constexpr (COMPACT) return sm.ulist[i];
+    else return i + 1 < D ? i + 1 : -1;
+  };
   uint32_t kvo[8], ksv[2];
+  auto job_offsets = [&]() {
 #pragma unroll
-  for (int cc = 0; cc < 8; ++cc) {
-    const int ch = slot_channel(8 * lo + cc);
-    kvo[cc] = ch >= 0 ? mul_apart((uint32_t)ch, kc_row) + 4u * (uint32_t)lq : kFar;
-  }
-  {
+    for (int cc = 0; cc < 8; ++cc) {
+      const int ch = slot_channel(8 * lo + cc);
+      kvo[cc] = ch >= 0 ? mul_apart((uint32_t)ch, kc_row) + 4u * (uint32_t)lq : kFar;
+    }
     const int c0a = slot_channel(as0), c1a = slot_channel(as1);
     ksv[0] = c0a >= 0 ? mul_apart((uint32_t)c0a, ks_row) + 2u * (uint32_t)at : kFar;
     ksv[1] = c1a >= 0 ? mul_apart((uint32_t)c1a, ks_row) + 2u * (uint32_t)at : kFar;
-  }
+  };
+  if constexpr (!COMPACT) job_offsets();
   const uint32_t c0o = tid < kBlock8 / 2 ? 4u * tid : kFar;
 
   auto kissue = [&](KStage8 &S, int p0, bool live) {
@@ -279,11 +304,18 @@ __global__ __launch_bounds__(kThreads8, 2) void decode8_kernel(dqk_cache c,
 
   const int nbc0 = nb == kChunk8 + 1 ? kChunk8 + 1 : min(kChunk8, nb);
   KStage8 S0, S1;
-  kissue(S0, t_begin, 0 < nbc0);
+  if constexpr (!COMPACT) kissue(S0, t_begin, 0 < nbc0);
 
   // ---------------------------------------------------------------- setup (whole workgroup)
   for (int e = tid; e < G * D / 4; e += kThreads8) sm.kept.w[e] = 0u;
+  if constexpr (COMPACT) {
+    if (tid < D) sm.ulist[tid] = uch >= 1 && uch < D ? uch : -1;
+  }
   block_barrier();
+  if constexpr (COMPACT) {   // the first block once the compact slots are known
+    job_offsets();
+    kissue(S0, t_begin, 0 < nbc0);
+  }
 #pragma unroll
   for (int k = 0; k < SJ; ++k) {
     const int e = tid + kThreads8 * k;
@@ -437,6 +469,9 @@ __global__ __launch_bounds__(kThreads8, 2) void decode8_kernel(dqk_cache c,
     asm volatile("" : "+v"(ones));
 #pragma unroll
     for (int kc = 0; kc < L::NKC; ++kc) {
+      if constexpr (COMPACT) {
+        if (kc >= nkc) break;   // wavefront-uniform
+      }
       const u32x4 al = *reinterpret_cast<const u32x4 *>(&B.a[wave].r[n][8 * (4 * kc + q)]);
       const u32x2 dk = *reinterpret_cast<const u32x2 *>(&B.y[wave][4 * kc + q][n >> 1][0]);
       const uint32_t l0 = pk_shl16(dk.x, shl2), h0 = pk_shr16(dk.x, shr2);
@@ -813,8 +848,8 @@ bool decode8_supported(const dqk_cache &c, int hq) {
   return c.capacity % 64 == 0 && hq == kG8 * c.num_kv_heads;
 }
 
-hipError_t launch_decode8(const dqk_cache &c, const float *q_prime, const int32_t *sel_idx, int hq,
-                          int keep, float scale2, int split, bool even, float *ws, float *out,
+hipError_t launch_decode8(const dqk_cache &c, const float *q_prime, const int32_t *sel_idx, bool shared,
+                          int hq, int keep, float scale2, int split, bool even, float *ws, float *out,
                           hipStream_t s) {
   const int nsplit = num_splits(c.capacity, split);
   // a caller's split of whole 128-token blocks covers exactly its tokens of
@@ -831,12 +866,25 @@ hipError_t launch_decode8(const dqk_cache &c, const float *q_prime, const int32_
     if (n > 0 && n < 4096 && items > n && items <= 2 * n) ncu = n;
   }
   const int ncu_q = ncu / units, ncu_r = ncu % units;
-  if (c.head_dim == 64)
-    hipLaunchKernelGGL((decode8_kernel<64>), grid, dim3(kThreads8), 0, s, c, q_prime, sel_idx, hq, grid3, keep,
-                       scale2, nsplit, bps, ncu_q, ncu_r, ws, out);
-  else
-    hipLaunchKernelGGL((decode8_kernel<128>), grid, dim3(kThreads8), 0, s, c, q_prime, sel_idx, hq, grid3, keep,
-                       scale2, nsplit, bps, ncu_q, ncu_r, ws, out);
+  // group-shared kept sets use compact slots: only the K chunks (32 slots each)
+  // that hold the keep - 1 kept channels other than 0 are worked on
+  const int nkc = shared ? (keep - 1 + 31) / 32 : c.head_dim / 32;
+  const dim3 block(kThreads8);
+  if (c.head_dim == 64) {
+    if (shared)
+      hipLaunchKernelGGL((decode8_kernel<64, true>), grid, block, 0, s, c, q_prime, sel_idx, hq, grid3, keep,
+                         scale2, nsplit, bps, ncu_q, ncu_r, nkc, ws, out);
+    else
+      hipLaunchKernelGGL((decode8_kernel<64, false>), grid, block, 0, s, c, q_prime, sel_idx, hq, grid3, keep,
+                         scale2, nsplit, bps, ncu_q, ncu_r, nkc, ws, out);
+  } else {
+    if (shared)
+      hipLaunchKernelGGL((decode8_kernel<128, true>), grid, block, 0, s, c, q_prime, sel_idx, hq, grid3, keep,
+                         scale2, nsplit, bps, ncu_q, ncu_r, nkc, ws, out);
+    else
+      hipLaunchKernelGGL((decode8_kernel<128, false>), grid, block, 0, s, c, q_prime, sel_idx, hq, grid3, keep,
+                         scale2, nsplit, bps, ncu_q, ncu_r, nkc, ws, out);
+  }
   return hipGetLastError();
 }
 

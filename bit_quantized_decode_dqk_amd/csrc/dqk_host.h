@@ -22,8 +22,8 @@ constexpr int kDefaultSplit = 1024; // bf16 decode split length when the caller 
 // Groups of four query heads share the sequence by length (each workgroup takes
 // an equal share of the current tokens): the default only fixes the number of
 // splits, about two workgroups per compute unit, with at least 256 tokens of
-// capacity per split.  `workgroups` is the number of workgroups per split index
-// (units times the four-head slices of a group).
+// capacity per split.  `workgroups` is the number of workgroups per split index:
+// the units (batch rows times KV heads), one workgroup each.
 inline int balanced_decode_split(int capacity, int workgroups) {
   int nsplit = 512 / workgroups;
   if (nsplit < 1) nsplit = 1;
@@ -155,16 +155,16 @@ hipError_t launch_append_select(const dqk_cache &c, const void *k_new, const voi
 hipError_t launch_decode(const dqk_cache &c, const float *q_prime, const int32_t *sel_idx,
                          bool shared, int hq, int keep, float sm_scale, int split, bool even,
                          float *out, float *ws, hipStream_t s);
-// the matrix-core decode: groups of a multiple of four query heads, capacity a multiple of 64;
-// partials to ws, or (out != nullptr, one split per row) the normalized output to out
+// the matrix-core decodes: groups of four (hq == 4 hkv) or eight (hq == 8 hkv) query
+// heads, per-head or group-shared kept sets, capacity a multiple of 64; partials to
+// ws, or (out != nullptr, one split per row) the normalized output to out
 bool decode4_supported(const dqk_cache &c, int hq);
 hipError_t launch_decode4(const dqk_cache &c, const float *q_prime, const int32_t *sel_idx,
                           bool shared, int hq, int keep, float scale2, int split, bool even,
                           float *ws, float *out, hipStream_t s);
-// the eight-head decode: hq == 8 hkv, per-head kept sets, capacity a multiple of 64
 bool decode8_supported(const dqk_cache &c, int hq);
-hipError_t launch_decode8(const dqk_cache &c, const float *q_prime, const int32_t *sel_idx, int hq,
-                          int keep, float scale2, int split, bool even, float *ws, float *out,
+hipError_t launch_decode8(const dqk_cache &c, const float *q_prime, const int32_t *sel_idx, bool shared,
+                          int hq, int keep, float scale2, int split, bool even, float *ws, float *out,
                           hipStream_t s);
 hipError_t launch_dequant(const dqk_cache &c, float *k_out, float *v_out, hipStream_t s);
 // every plane of src re-strided into dst (same batch, KV heads, head_dim; larger capacity)

@@ -445,9 +445,8 @@ def test_decode_group4_chunk_sizes(orc):
 def test_decode_group4_unit_counts(orc, hq, hkv, lens):
     """Groups of four and of eight with (row, KV head) counts that are not
     multiples of eight: the splits of one row and KV head run on different parts
-    of the chip, and the combine joins the partials.  Groups of eight also run
-    with group-shared kept sets: two four-head workgroups per work item, with the
-    grid padded to whole groups of eight work items."""
+    of the chip, and the combine joins the partials; groups of eight also with
+    group-shared kept sets (the eight-head kernel's compact slots)."""
     wl = W.custom(f"g4-u{hkv}", 30 + hkv, len(lens), hq, hkv, 128, lens, 4032, "bf16",
                   log_uniform_key_scales=True)
     decode_case(orc, wl, splits=(0, 64, 256, 1024))
