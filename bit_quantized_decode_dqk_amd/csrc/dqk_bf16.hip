@@ -6,8 +6,9 @@
 // A work item is one (batch row, KV head, split); it serves every query head of
 // the GQA group so each key/value byte is read once.  64-token tiles of K and V
 // are staged through LDS with coalesced 16-byte loads (rows padded by one dword
-// against bank conflicts); lanes own (token, head) pairs for the logits and
-// (channel, part) pairs for the weighted sum.  The split partials use the same
+// against bank conflicts); the next tile's loads are in flight in registers
+// while the current one is worked on.  Lanes own (token, head) pairs for the
+// logits and (channel, part) pairs for the weighted sum.  The split partials use the same
 // workspace format and combine kernel as the 2-bit decode.
 #include "dqk_internal.h"
 
@@ -63,22 +64,37 @@ __global__ __launch_bounds__(kThreads) void bf16_decode_kernel(
 #pragma unroll
   for (int h = 0; h < G; ++h) o_acc[h] = 0.0f;
 
+  // K and V rows tc..tc+kTile-1 as 16-byte pieces (D/8 per row), PPT per thread;
+  // rows at or past t_end are zeros
+  constexpr int PPT = kTile * (D / 8) / kThreads;
+  static_assert(PPT * kThreads == kTile * (D / 8), "whole pieces per thread");
+  uint4 pk[PPT], pv[PPT];
+  auto fetch = [&](int tc) {
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) {
+      const int e = tid + kThreads * j, r = e / (D / 8), piece = e % (D / 8);
+      pk[j] = pv[j] = make_uint4(0, 0, 0, 0);
+      if (tc + r < t_end) {
+        pk[j] = k4[(size_t)(tc + r) * (D / 8) + piece];
+        pv[j] = v4[(size_t)(tc + r) * (D / 8) + piece];
+      }
+    }
+  };
+  fetch(t_begin);
   for (int tc = t_begin; tc < t_end; tc += kTile) {
     const int n = min(kTile, t_end - tc);
-    // stage K and V rows tc..tc+n-1 (16-byte pieces, D/8 per row)
-    for (int e = tid; e < kTile * (D / 8); e += kThreads) {
-      const int r = e / (D / 8), piece = e % (D / 8);
-      uint4 kv = make_uint4(0, 0, 0, 0), vv = kv;
-      if (r < n) {
-        kv = k4[(size_t)(tc + r) * (D / 8) + piece];
-        vv = v4[(size_t)(tc + r) * (D / 8) + piece];
-      }
+    // stage this tile (the previous one is no longer read: the loop ends with a
+    // barrier), then put the next tile's loads in flight
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) {
+      const int e = tid + kThreads * j, r = e / (D / 8), piece = e % (D / 8);
       uint32_t *kr = &sm.kt[r][piece * 4];
       uint32_t *vr = &sm.vt[r][piece * 4];
-      kr[0] = kv.x; kr[1] = kv.y; kr[2] = kv.z; kr[3] = kv.w;
-      vr[0] = vv.x; vr[1] = vv.y; vr[2] = vv.z; vr[3] = vv.w;
+      kr[0] = pk[j].x; kr[1] = pk[j].y; kr[2] = pk[j].z; kr[3] = pk[j].w;
+      vr[0] = pv[j].x; vr[1] = pv[j].y; vr[2] = pv[j].z; vr[3] = pv[j].w;
     }
     __syncthreads();
+    if (tc + kTile < t_end) fetch(tc + kTile);
     // logits: lane pair (token r, head h)
     for (int e = tid; e < kTile * G; e += kThreads) {
       const int r = e % kTile, h = e / kTile;
