@@ -6,6 +6,8 @@ heads of ||o - o_ref||_inf / ||o_ref||_inf): attention outputs.  Inputs are the
 seeded synthetic workloads, at sizes the oracle finishes in seconds that still
 span several splits and a ragged tail.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -16,6 +18,12 @@ from gpu_util import (REL_TOL, assert_same_cache, dev_f32, dev_i32, dev_input, p
                       rel_err, say)
 
 pytestmark = pytest.mark.gpu
+
+
+def _env_int(name: str, default: int) -> int:
+    """Case count or seed of the seeded random sweeps below (environment override, for
+    longer runs than the default suite's)."""
+    return int(os.environ.get(name, default))
 
 
 def _counts(wl, pos, n):
@@ -118,7 +126,9 @@ def _random_append_cases(n: int, seed: int):
     return out
 
 
-@pytest.mark.parametrize("case", _random_append_cases(12, 77), ids=lambda c: f"a{c[0]}")
+@pytest.mark.parametrize("case", _random_append_cases(_env_int("DQK_RANDOM_APPEND_CASES", 12),
+                                                    _env_int("DQK_RANDOM_SEED", 77)),
+                         ids=lambda c: f"a{c[0]}")
 def test_append_random_chunks(orc, case):
     """Random chunk sequences (one-token, small and bulk appends, so both the
     held-column and the bulk forms run) with ragged per-row counts, some rows
@@ -358,7 +368,8 @@ def _random_cases(n: int, seed: int):
     return out
 
 
-@pytest.mark.parametrize("case", _random_cases(24, 2024), ids=lambda c: f"r{c[0]}")
+@pytest.mark.parametrize("case", _random_cases(_env_int("DQK_RANDOM_CASES", 24), _env_int("DQK_RANDOM_SEED", 2024)),
+                         ids=lambda c: f"r{c[0]}")
 def test_decode_random_shapes(orc, case):
     """A seeded sweep of random shapes through append, select and decode against the
     oracle: planes bit-exact, q' and kept sets bit-exact, outputs within 2e-3 (an
