@@ -298,7 +298,7 @@ dqk_status dqk_bf16_decode_attention(const uint16_t *q, const uint16_t *k, const
                                      int32_t split, float *out, void *workspace, size_t ws_bytes,
                                      dqk_stream_t stream) {
   if (!q || !k || !v || !lengths || !out) return DQK_ERR_INVALID;
-  if (!aligned16(k) || !aligned16(v)) return DQK_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return DQK_ERR_INVALID;
   if (batch <= 0 || ld_t <= 0 || hq <= 0 || hkv <= 0 || hq % hkv != 0) return DQK_ERR_INVALID;
   if (!supported_dim(d) || !supported_group(hq, hkv)) return DQK_ERR_UNSUPPORTED;
   if (!isfinite(sm_scale) || !valid_split(split)) return DQK_ERR_INVALID;

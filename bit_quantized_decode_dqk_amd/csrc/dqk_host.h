@@ -13,7 +13,7 @@
 namespace dqk {
 
 constexpr int kGroup = 32;          // tokens (keys) or channels (values) per scale
-constexpr int kDefaultSplit = 1024; // bf16 decode split length when the caller passes 0
+constexpr int kDefaultSplit = 2048; // bf16 decode split length when the caller passes 0
 
 // Default 2-bit decode split: the capacity spread over about two resident
 // workgroups per compute unit on 256 compute units, rounded down to 256-token

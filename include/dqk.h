@@ -253,7 +253,10 @@ dqk_status dqk_dequant_reference(const dqk_cache *cache, float *k_out, float *v_
  * values, no transforms, no quantization, fp32 accumulation.
  * q: [batch][hq][d] bf16; k, v: [batch][hkv][ld_t][d] bf16 (token-major);
  * lengths: [batch] i32 (<= ld_t); out: [batch][hq][d] fp32; workspace as for
- * dqk_decode_attention, sized by dqk_bf16_decode_workspace_bytes. */
+ * dqk_decode_attention, sized by dqk_bf16_decode_workspace_bytes.  q, k and v
+ * must be 16-byte aligned (DQK_ERR_INVALID otherwise).  The logits are fp32 sums
+ * of the exact bf16 products; with the same inputs the result does not depend
+ * on the split beyond fp32 rounding. */
 dqk_status dqk_bf16_decode_workspace_bytes(int32_t batch, int32_t hq, int32_t hkv,
                                            int32_t head_dim, int32_t ld_t,
                                            int32_t split_tokens, size_t *out_bytes);

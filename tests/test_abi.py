@@ -244,12 +244,15 @@ def test_bf16_decode_validation_without_gpu():
     L = M.lib()
     out = C.c_size_t(0)
     assert L.dqk_bf16_decode_workspace_bytes(1, 32, 8, 128, 131072, 0, C.byref(out)) == OK
-    assert out.value == 8 * 128 * 4 * 132 * 4
+    assert out.value == 8 * 64 * 4 * 132 * 4    # 2048-token splits by default
     assert L.dqk_bf16_decode_workspace_bytes(1, 32, 8, 96, 1024, 0, C.byref(out)) == UNSUPPORTED
     args = [0x20000, 0x30000, 0x40000, 0x50000, 1, 32, 8, 128, 1024, 0.1, 0, 0x60000, 0x70000,
             1 << 30, None]
     bad = list(args)
     bad[1] = 0x30004                      # misaligned keys
+    assert L.dqk_bf16_decode_attention(*bad) == INVALID
+    bad = list(args)
+    bad[0] = 0x20008                      # misaligned queries
     assert L.dqk_bf16_decode_attention(*bad) == INVALID
     bad = list(args)
     bad[12] = None
