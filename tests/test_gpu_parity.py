@@ -852,6 +852,32 @@ def test_bf16_decode_matches_plain_attention(orc, lens, sm_mult):
         assert err <= REL_TOL
 
 
+@pytest.mark.parametrize("hq,hkv,d,lens", [(8, 8, 64, [700, 33]), (16, 8, 128, [1500]),
+                                          (16, 4, 64, [2000, 1]), (64, 8, 128, [900, 0]),
+                                          (32, 4, 64, [1200, 95])])
+def test_bf16_decode_group_sizes(orc, hq, hkv, d, lens):
+    """The comparator for every group size (1, 2, 4, 8) and head dimension, with
+    ragged, one-token and empty rows and tiles cut by the split end."""
+    cap = (max(lens) + 63) // 64 * 64 + 64
+    wl = W.custom(f"bf16g{hq}-{hkv}-{d}", 27, len(lens), hq, hkv, d, lens, cap, "bf16",
+                  log_uniform_key_scales=True, student_t_queries=(hq == 8 * hkv))
+    say("bf16 decode", hq, hkv, d, lens)
+    k, v = W.prefill_kv(wl)
+    q = W.queries(wl)
+    sm = W.default_sm_scale(wl.d) * 0.05
+    ref = orc.plain_attention(q, k, v, list(wl.ctx), sm)
+    for sp in (0, 32, 96, 1024):
+        out = M.bf16_decode_attention(dev_input(q, "bf16"), dev_input(k, "bf16"),
+                                      dev_input(v, "bf16"), dev_i32(wl.ctx), sm,
+                                      split_tokens=sp).cpu().numpy()
+        err = rel_err(out, ref)
+        say(f"  split {sp}: {err:.3e}")
+        assert err <= REL_TOL
+        for bb, n in enumerate(lens):
+            if n == 0:
+                assert not out[bb].any()
+
+
 # ----------------------------------------------------------------------------- group-shared selection
 
 @pytest.mark.parametrize("name", W.WORKLOADS)
