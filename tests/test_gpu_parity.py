@@ -878,6 +878,25 @@ def test_bf16_decode_group_sizes(orc, hq, hkv, d, lens):
                 assert not out[bb].any()
 
 
+def test_bf16_decode_ctx128k_full(orc):
+    """The comparator at the bench's context length (131072 tokens, GQA 8/2 heads, bf16
+    inputs with the 128K workload's key scales) against the oracle's plain fp64 attention,
+    every output, at the default split and a split that cuts the last tile."""
+    wl = W.custom("bf16-128k", 29, 1, 8, 2, 128, [131072], 131072, "bf16",
+                  log_uniform_key_scales=True)
+    k, v = W.prefill_kv(wl)
+    q = W.queries(wl)
+    sm = W.default_sm_scale(wl.d)
+    ref = orc.plain_attention(q, k, v, list(wl.ctx), sm)
+    kd, vd = dev_input(k, "bf16"), dev_input(v, "bf16")
+    for sp in (0, 3040):
+        out = M.bf16_decode_attention(dev_input(q, "bf16"), kd, vd, dev_i32(wl.ctx), sm,
+                                      split_tokens=sp).cpu().numpy()
+        err = rel_err(out, ref)
+        say(f"bf16 decode 128K split {sp}: max rel err {err:.3e}")
+        assert err <= REL_TOL
+
+
 # ----------------------------------------------------------------------------- group-shared selection
 
 @pytest.mark.parametrize("name", W.WORKLOADS)
